@@ -1,0 +1,233 @@
+/*
+ * ffnq.h -- C ABI of libffnq: the quantized-weight gated FFN of a transformer
+ * layer and the MoE routed half that reuses it, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method (docs.rs pages of the `turbospark-runtime` crate):
+ *   [gemma4/shared_expert.rs]  `encode_shared_expert_branch` and
+ *                              `encode_shared_expert_branch_batched`
+ *   [qwen/moe_batch.rs]        module doc and `encode_qwen_layer_moe_batched`
+ *   [llama/dense.rs]           module doc (the FFN equation) and
+ *                              `encode_llama_layer_dense`
+ *
+ * General conventions (every entry point):
+ *   - Return value: FFNQ_OK (0) or a negative FFNQ_ERR_* code.  Every argument
+ *     check runs on the host before anything is enqueued, so an INVALID,
+ *     UNSUPPORTED, CAPACITY or WORKSPACE return enqueues nothing.  FFNQ_ERR_HIP
+ *     means a launch failed; kernels of the same call enqueued before the
+ *     failing one may already be on the stream.
+ *   - Pointers named "device" are HIP device pointers; the ffnq_qmat / ffnq_ffn
+ *     structs themselves live in host memory and are read during the call only.
+ *   - Every device pointer must be 16-byte aligned (128-bit loads).  Tensors are
+ *     contiguous and row-major, with no strides.
+ *   - Ownership: the caller allocates every buffer.  The library allocates,
+ *     frees and synchronises nothing and keeps no state between calls.  Calls
+ *     are asynchronous on `stream`; the caller keeps every buffer alive (and
+ *     unmodified, for inputs) until the stream's work has completed -- the ABI
+ *     form of the pages' rule that weight memory must outlive in-flight work
+ *     ([gemma4/shared_expert.rs], doc of `encode_shared_expert_branch`).
+ *   - Workspace: calls that take (ws, ws_bytes) write the bytes they need to
+ *     *ws_bytes and return FFNQ_OK without enqueuing anything when ws == NULL.
+ *     With ws != NULL, *ws_bytes is the workspace size the caller provides;
+ *     FFNQ_ERR_WORKSPACE if it is smaller than required.  Its contents on entry
+ *     do not matter.  Concurrent calls need distinct workspaces.
+ *   - m == 0 (no tokens) is a no-op that returns FFNQ_OK after the checks.
+ *   - bf16 is the 16-bit brain float (upper half of an IEEE binary32), passed as
+ *     uint16_t storage.  Activations are bf16 at the ABI; every intermediate is
+ *     fp32 and outputs are rounded to bf16 once, to nearest even.
+ */
+#ifndef FFNQ_H
+#define FFNQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define FFNQ_OK                 0
+#define FFNQ_ERR_INVALID       -1  /* NULL pointer, width <= 0, bad alignment, aliasing, K not a multiple of 64 */
+#define FFNQ_ERR_UNSUPPORTED   -2  /* unknown fmt/act/tail, routed experts not INT4-affine, slot_cap > 32, ... */
+#define FFNQ_ERR_CAPACITY      -3  /* slot_cap < top_k: not even one token fits a sub-batch */
+#define FFNQ_ERR_WORKSPACE     -4  /* workspace or plan buffer too small */
+#define FFNQ_ERR_HIP           -5  /* a kernel launch failed */
+
+/* ---- weight formats ------------------------------------------------------
+ * FFNQ_FMT_INT8_ROW: symmetric per-output-row INT8.
+ *   q: int8  [n][k]      w[i][j] = s[i] * q[i][j]
+ *   s: fp32  [n]
+ *   z: NULL
+ *   k must be a multiple of 64.
+ * FFNQ_FMT_INT4_AFFINE_G64: affine INT4, groups of 64 consecutive inputs.
+ *   q: uint8 [n][k/2]    code(i,j) = (q[i][j/2] >> (4*(j&1))) & 0xF
+ *                        (even j in the low nibble)
+ *   s: bf16  [n][k/64]   w[i][j] = s[i][j/64] * (code(i,j) - z[i][j/64])
+ *   z: bf16  [n][k/64]
+ *   k must be a multiple of 128 for the GPU kernels (64 defines the format;
+ *   k % 128 == 64 is refused with FFNQ_ERR_UNSUPPORTED).
+ * The pages name the routed blob layout "Affine" ([qwen/moe_batch.rs],
+ * refusal of non-Affine layouts in `encode_qwen_layer_moe_batched`) and the
+ * shared expert "INT8" ([gemma4/shared_expert.rs], branch doc); the exact bit
+ * layouts above are this library's reading.
+ */
+#define FFNQ_FMT_INT8_ROW         1
+#define FFNQ_FMT_INT4_AFFINE_G64  2
+
+/* ---- gated activation, act = f(gate) * up  --------------------------------
+ * The gate projection is the operand passed through f ([llama/dense.rs]: the
+ * `encode_silu_mul` / `encode_gelu_mul` call takes ffn_gate first).
+ *   SILU:      f(v) = v / (1 + exp(-v))
+ *   GELU_TANH: f(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ */
+#define FFNQ_ACT_SILU       1
+#define FFNQ_ACT_GELU_TANH  2
+
+/* ---- tails (what happens to h = down(act)) -------------------------------- */
+#define FFNQ_TAIL_NONE          0  /* h_out = bf16(h) */
+#define FFNQ_TAIL_RESIDUAL      1  /* x_res = bf16(x_res + h)   [llama/dense.rs] residual add */
+#define FFNQ_TAIL_RMSNORM       2  /* out = bf16(h / sqrt(mean(h^2) + eps) * w)   [gemma4/shared_expert.rs] */
+#define FFNQ_TAIL_SIGMOID_GATE  3  /* h_out = bf16(h * sigmoid(<w_gate, x>))      [qwen/moe_batch.rs] shared expert */
+
+/* Ceiling on expert slots per routed sub-batch: the pages' 32-pointer argument
+ * buffer ([qwen/moe_batch.rs], module doc and the slot-count refusal). */
+#define FFNQ_MAX_SLOTS 32
+/* Largest expert count the router kernel holds per token. */
+#define FFNQ_MAX_EXPERTS 1024
+
+/* One quantized matrix of n output rows and k inputs.  For stacked expert
+ * tensors the pointers address expert 0 and expert e starts at
+ *   q + e*n*k (INT8) or q + e*n*k/2 (INT4) bytes,
+ *   s + e*n   (INT8, fp32) or s + e*n*(k/64) (INT4, bf16) elements, z likewise. */
+typedef struct ffnq_qmat {
+    int32_t fmt;      /* FFNQ_FMT_* */
+    int32_t n;        /* output rows */
+    int32_t k;        /* inputs (columns) */
+    const void* q;    /* device: codes */
+    const void* s;    /* device: scales */
+    const void* z;    /* device: zero points (INT4) or NULL (INT8) */
+} ffnq_qmat;
+
+/* A gated FFN: gate and up are [inter][hidden], down is [hidden][inter]
+ * ([gemma4/shared_expert.rs]: gate/up GEMVs take rows=inter, cols=hidden; the
+ * down GEMV takes rows=hidden, cols=inter).  gate and up must share a format;
+ * down may use another (per-tensor block type, [llama/dense.rs] module doc). */
+typedef struct ffnq_ffn {
+    ffnq_qmat gate, up, down;
+} ffnq_ffn;
+
+/* ---- ffnq_dense ------------------------------------------------------------
+ * Dense FFN half of a layer, for m token-major rows ([llama/dense.rs], the
+ * module-doc equation and `encode_llama_layer_dense`):
+ *     h = down( f(gate @ x_t) * (up @ x_t) )
+ *   tail RESIDUAL: out[t] = bf16(out[t] + h)       (out is the residual stream, in/out)
+ *   tail RMSNORM:  out[t] = bf16(rmsnorm(h) * norm_w)  (out is written only)
+ * hidden, inter: the FFN widths (the dense width is intermediate_size; a width
+ *   of 0 is refused, [llama/dense.rs] module doc).  Must match the ffn shapes.
+ * x:      device bf16 [m][hidden]; must not overlap out.
+ * out:    device bf16 [m][hidden].
+ * norm_w: device bf16 [hidden] for RMSNORM, else ignored (may be NULL).
+ * eps:    RMSNorm epsilon (>= 0), added to the mean of squares inside the sqrt.
+ * ws:     device workspace (see conventions), or NULL to query *ws_bytes.
+ */
+int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
+               const uint16_t* x, uint16_t* out, const uint16_t* norm_w, float eps,
+               void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* ---- ffnq_shared_expert ----------------------------------------------------
+ * The shared (dense) expert branch: the same gated FFN with the shared
+ * expert's tails, for m rows at once ([gemma4/shared_expert.rs]
+ * `encode_shared_expert_branch_batched`; [qwen/moe_batch.rs] the gated shared
+ * expert inside `encode_qwen_layer_moe_batched`):
+ *   tail RMSNORM:      h_out[t] = bf16(rmsnorm(h) * aux)          aux = norm weight bf16 [hidden]
+ *   tail SIGMOID_GATE: h_out[t] = bf16(h * sigmoid(<aux, x_t>))   aux = gate vector bf16 [hidden],
+ *                      the logit is an fp32 dot product over hidden
+ *   tail NONE:         h_out[t] = bf16(h)                          aux ignored
+ * h_out:  device bf16 [m][hidden]; must not overlap x.  With SIGMOID_GATE this
+ *         is the seed that ffnq_moe_routed_batched starts its accumulator at.
+ */
+int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
+                       const uint16_t* x, uint16_t* h_out, const uint16_t* aux, float eps,
+                       void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* ---- ffnq_moe_route ----------------------------------------------------------
+ * Router top-k and the expert-union plan, entirely on the device
+ * ([qwen/moe_batch.rs]: the host top-k over read-back logits with
+ * `router_topk_gemma4`, the cap min(slots, 32) and the sub-batch loop of
+ * `encode_qwen_layer_moe_batched`; the module doc's union bound).
+ *
+ * logits:       device fp32 [m][n_experts].
+ * expert_scale: device fp32 [n_experts] per-expert multiplier, or NULL (= ones).
+ * top_k:        1 <= top_k <= n_experts; n_experts <= FFNQ_MAX_EXPERTS.
+ * slot_cap:     expert slots per sub-batch; top_k <= slot_cap <= FFNQ_MAX_SLOTS.
+ * topk_ids:     device int32 [m][top_k]: expert of pair p = t*top_k + r (pair
+ *               order: token-major, rank within).
+ * topk_w:       device fp32 [m][top_k]: route weights.
+ * plan:         device int32 buffer of plan_bytes >= 4*FFNQ_PLAN_INTS(m, top_k).
+ *
+ * Selection: experts are ranked by logit, descending; equal logits go to the
+ * lower index; NaN ranks as -inf.  Rank 0 is the largest logit.
+ * Weights: w_r = exp(l_r - l_0) / sum_{r'<k} exp(l_r' - l_0) * scale[e_r]
+ * (softmax over all experts renormalised over the selected ones; the full
+ * denominator cancels).  A selected logit equal to l_0 contributes exp(0)=1
+ * (this also fixes the all-(-inf) and +inf cases); NaN counts as -inf.
+ *
+ * Plan (all int32, fixed offsets sized for the worst case; S = sub-batches,
+ * U = total union entries; unused entries are -1):
+ *   [0]                               n_sub = S
+ *   sub_tok_begin  [m+1]              token range of sub-batch b: [begin[b], begin[b+1])
+ *   sub_union_begin[m+1]              its union entries: [ub[b], ub[b+1]) of union_expert
+ *   union_expert   [m*k]              each sub-batch's union in first-appearance pair order;
+ *                                     the slot of an expert is its index within its sub-batch
+ *   pair_slot      [m*k]              slot (within its sub-batch) of pair p
+ *   slot_pair_begin[m*k+1]            pairs of global union entry g: slot_pairs[spb[g] .. spb[g+1])
+ *   slot_pairs     [m*k]              pair indices grouped by union entry, ascending within
+ * Sub-batches are greedy and maximal: starting at token s, tokens are added
+ * while the union of their experts stays <= slot_cap.
+ */
+#define FFNQ_PLAN_INTS(m, k) (1 + 2 * ((m) + 1) + 4 * (m) * (k) + 1)
+#define FFNQ_PLAN_N_SUB(m, k)           0
+#define FFNQ_PLAN_SUB_TOK_BEGIN(m, k)   1
+#define FFNQ_PLAN_SUB_UNION_BEGIN(m, k) ((m) + 2)
+#define FFNQ_PLAN_UNION_EXPERT(m, k)    (2 * (m) + 3)
+#define FFNQ_PLAN_PAIR_SLOT(m, k)       (2 * (m) + 3 + (m) * (k))
+#define FFNQ_PLAN_SLOT_PAIR_BEGIN(m, k) (2 * (m) + 3 + 2 * (m) * (k))
+#define FFNQ_PLAN_SLOT_PAIRS(m, k)      (2 * (m) + 4 + 3 * (m) * (k))
+
+int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_experts,
+                   int top_k, int slot_cap, int32_t* topk_ids, float* topk_w,
+                   int32_t* plan, size_t plan_bytes, hipStream_t stream);
+
+/* ---- ffnq_moe_routed_batched -----------------------------------------------
+ * The routed half for m tokens ([qwen/moe_batch.rs]: phase 1, the fused and
+ * seeded phase 2 and the raw residual add of `encode_qwen_layer_moe_batched`):
+ *   phase 1, per pair p = t*k + r with expert e = topk_ids[p]:
+ *       act_p = f(gate_e @ x_t) * (up_e @ x_t)
+ *   phase 2, per token t and output i, the fp32 accumulator is SEEDED:
+ *       acc = seed[t][i]  (0 when seed == NULL)
+ *       for r = 0..k-1:  acc += topk_w[t*k+r] * (down_e @ act_{t*k+r})[i]
+ *   tail: resid[t][i] = bf16(resid[t][i] + acc)   (one raw residual add, no norm)
+ * experts:   stacked [n_experts] INT4-affine gate/up [moe_inter][hidden] and
+ *            down [hidden][moe_inter]; other formats are refused (UNSUPPORTED),
+ *            as the pages refuse non-Affine blobs for the batched pass.
+ * x:         device bf16 [m][hidden]; must not overlap resid.
+ * topk_ids, topk_w, plan: as written by ffnq_moe_route for the same m, k.
+ * seed:      device bf16 [m][hidden] (the gated shared expert) or NULL.
+ * resid:     device bf16 [m][hidden], in/out.
+ * Expert ids outside [0, n_experts) and plan entries outside their ranges are
+ * skipped on the device rather than dereferenced.
+ */
+int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter,
+                            int m, int top_k, int act, const uint16_t* x,
+                            const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
+                            const uint16_t* seed, uint16_t* resid,
+                            void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* ffnq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FFNQ_H */
