@@ -46,6 +46,10 @@
 extern "C" {
 #endif
 
+#ifndef FFNQ_API
+#define FFNQ_API __attribute__((visibility("default")))
+#endif
+
 /* ---- status codes ------------------------------------------------------- */
 #define FFNQ_OK                 0
 #define FFNQ_ERR_INVALID       -1  /* NULL pointer, width <= 0, bad alignment, aliasing, K not a multiple of 64 */
@@ -131,7 +135,7 @@ typedef struct ffnq_ffn {
  * eps:    RMSNorm epsilon (>= 0), added to the mean of squares inside the sqrt.
  * ws:     device workspace (see conventions), or NULL to query *ws_bytes.
  */
-int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
+FFNQ_API int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
                const uint16_t* x, uint16_t* out, const uint16_t* norm_w, float eps,
                void* ws, size_t* ws_bytes, hipStream_t stream);
 
@@ -147,7 +151,7 @@ int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int t
  * h_out:  device bf16 [m][hidden]; must not overlap x.  With SIGMOID_GATE this
  *         is the seed that ffnq_moe_routed_batched starts its accumulator at.
  */
-int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
+FFNQ_API int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
                        const uint16_t* x, uint16_t* h_out, const uint16_t* aux, float eps,
                        void* ws, size_t* ws_bytes, hipStream_t stream);
 
@@ -195,7 +199,7 @@ int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int m, int ac
 #define FFNQ_PLAN_SLOT_PAIR_BEGIN(m, k) (2 * (m) + 3 + 2 * (m) * (k))
 #define FFNQ_PLAN_SLOT_PAIRS(m, k)      (2 * (m) + 4 + 3 * (m) * (k))
 
-int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_experts,
+FFNQ_API int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_experts,
                    int top_k, int slot_cap, int32_t* topk_ids, float* topk_w,
                    int32_t* plan, size_t plan_bytes, hipStream_t stream);
 
@@ -218,14 +222,14 @@ int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_
  * Expert ids outside [0, n_experts) and plan entries outside their ranges are
  * skipped on the device rather than dereferenced.
  */
-int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter,
+FFNQ_API int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter,
                             int m, int top_k, int act, const uint16_t* x,
                             const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
                             const uint16_t* seed, uint16_t* resid,
                             void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
-const char* ffnq_status_string(int status);
+FFNQ_API const char* ffnq_status_string(int status);
 
 #ifdef __cplusplus
 }

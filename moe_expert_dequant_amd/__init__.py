@@ -1,0 +1,184 @@
+"""Python binding of libffnq (quantized gated FFN + MoE routed half, gfx950).
+
+A thin ctypes layer over the C ABI in include/ffnq.h: it marshals torch device
+tensors into pointers and the current HIP stream, allocates workspaces with
+torch, and raises on a non-OK status.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback path.  If libffnq.so has not
+been built, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+from .build import LIB, build  # noqa: F401
+
+FMT_INT8_ROW = 1
+FMT_INT4_AFFINE_G64 = 2
+ACT_SILU = 1
+ACT_GELU_TANH = 2
+TAIL_NONE = 0
+TAIL_RESIDUAL = 1
+TAIL_RMSNORM = 2
+TAIL_SIGMOID_GATE = 3
+
+OK = 0
+STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
+EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_status_string")
+
+
+def plan_ints(m: int, k: int) -> int:
+    """int32 entries of a routing plan for m tokens at top-k (FFNQ_PLAN_INTS)."""
+    return 1 + 2 * (m + 1) + 4 * m * k + 1
+
+
+class FfnqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class QMat(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("n", C.c_int32), ("k", C.c_int32),
+                ("q", C.c_void_p), ("s", C.c_void_p), ("z", C.c_void_p)]
+
+
+class Ffn(C.Structure):
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libffnq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"libffnq.so is not built ({LIB}); run __graft_entry__.build()")
+        L = C.CDLL(LIB)
+        vp, i32, f32, sz = C.c_void_p, C.c_int, C.c_float, C.POINTER(C.c_size_t)
+        FP = C.POINTER(Ffn)
+        L.ffnq_dense.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
+        L.ffnq_shared_expert.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
+        L.ffnq_moe_route.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
+        L.ffnq_moe_routed_batched.argtypes = [FP, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for f in ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched"):
+            getattr(L, f).restype = C.c_int
+        L.ffnq_status_string.argtypes = [C.c_int]
+        L.ffnq_status_string.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def qmat(fmt: int, n: int, k: int, q, s, z=None) -> QMat:
+    return QMat(fmt, n, k, _ptr(q), _ptr(s), _ptr(z))
+
+
+def ffn_struct(mats: dict) -> Ffn:
+    """mats: {gate, up, down} -> dict(fmt, n, k, q, s, z) with torch device tensors (or pointers)."""
+    return Ffn(*(qmat(mats[n]["fmt"], mats[n]["n"], mats[n]["k"], mats[n]["q"], mats[n]["s"], mats[n].get("z"))
+                 for n in ("gate", "up", "down")))
+
+
+def _check(fn: str, rc: int):
+    if rc != OK:
+        raise FfnqError(fn, rc)
+
+
+class Workspace:
+    """A reusable device workspace that grows on demand (torch allocation)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf, self.buf.numel()
+
+
+def _ws(fn, args, ws: Workspace | None):
+    size = C.c_size_t(0)
+    rc = fn(*args, None, C.byref(size), None)
+    _check(fn.__name__, rc)
+    ws = ws or Workspace()
+    buf, n = ws.get(size.value)
+    return buf, C.c_size_t(n)
+
+
+def dense(ffn: Ffn, hidden: int, inter: int, m: int, act: int, tail: int, x, out, norm_w=None,
+          eps: float = 1e-6, ws: Workspace | None = None, stream=None):
+    """ffnq_dense: out is the residual stream (RESIDUAL, in/out) or the norm output (RMSNORM)."""
+    L = lib()
+    args = (C.byref(ffn), hidden, inter, m, act, tail, _ptr(x), _ptr(out), _ptr(norm_w), eps)
+    buf, n = _ws(L.ffnq_dense, args, ws)
+    _check("ffnq_dense", L.ffnq_dense(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+def shared_expert(ffn: Ffn, hidden: int, inter: int, m: int, act: int, tail: int, x, h_out, aux=None,
+                  eps: float = 1e-6, ws: Workspace | None = None, stream=None):
+    L = lib()
+    args = (C.byref(ffn), hidden, inter, m, act, tail, _ptr(x), _ptr(h_out), _ptr(aux), eps)
+    buf, n = _ws(L.ffnq_shared_expert, args, ws)
+    _check("ffnq_shared_expert", L.ffnq_shared_expert(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+def moe_route(logits, m: int, n_experts: int, top_k: int, slot_cap: int, topk_ids, topk_w, plan,
+              expert_scale=None, stream=None):
+    L = lib()
+    nbytes = plan.numel() * plan.element_size() if hasattr(plan, "numel") else 0
+    _check("ffnq_moe_route", L.ffnq_moe_route(_ptr(logits), _ptr(expert_scale), m, n_experts, top_k, slot_cap,
+                                              _ptr(topk_ids), _ptr(topk_w), _ptr(plan), nbytes, _stream(stream)))
+
+
+def moe_routed_batched(experts: Ffn, n_experts: int, hidden: int, moe_inter: int, m: int, top_k: int, act: int,
+                       x, topk_ids, topk_w, plan, seed, resid, ws: Workspace | None = None, stream=None):
+    L = lib()
+    args = (C.byref(experts), n_experts, hidden, moe_inter, m, top_k, act, _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+            _ptr(plan), _ptr(seed), _ptr(resid))
+    buf, n = _ws(L.ffnq_moe_routed_batched, args, ws)
+    _check("ffnq_moe_routed_batched", L.ffnq_moe_routed_batched(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+def workspace_bytes(kind: str, *args) -> int:
+    """Workspace query (ws == NULL) for 'dense', 'shared' or 'routed' with the call's leading arguments."""
+    L = lib()
+    fn = {"dense": L.ffnq_dense, "shared": L.ffnq_shared_expert, "routed": L.ffnq_moe_routed_batched}[kind]
+    size = C.c_size_t(0)
+    _check(fn.__name__, fn(*args, None, C.byref(size), None))
+    return size.value
+
+
+def to_device(mat: dict, device="cuda") -> dict:
+    """numpy matrix dict (fmt, n, k, q, s, z) -> the same with torch device tensors."""
+    def t(a):
+        if a is None:
+            return None
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device)
+        return torch.from_numpy(a).to(device)
+    return dict(fmt=mat["fmt"], n=mat["n"], k=mat["k"], q=t(mat["q"]), s=t(mat["s"]), z=t(mat.get("z")))

@@ -1,0 +1,189 @@
+// route.h -- router top-k and the expert-union plan, on the device.
+//
+// The pages read the whole batch's router logits back to the host and run the
+// top-k per token there ([qwen/moe_batch.rs], encode_qwen_layer_moe_batched:
+// read_f32_buffer_at + router_topk_gemma4), then plan sub-batches whose expert
+// union fits the slot cap (next_routed_sub_batch / plan_and_stream_union).
+// Here both steps run in one workgroup so the layer has no host round trip:
+// the waves select each token's experts in parallel, then wave 0 walks the
+// tokens in order to build the greedy union plan.
+#pragma once
+#include "device.h"
+
+namespace ffnq {
+
+constexpr int kMaxExperts = 1024;   // logits per token held in registers: 16 per lane
+constexpr int kMaxSlots = 32;
+
+struct RouteParams {
+    const float* logits;    // [m][E]
+    const float* scale;     // [E] or null
+    int m, E, k, cap;
+    int32_t* ids;           // [m][k]
+    float* w;               // [m][k]
+    int32_t* plan;
+};
+
+// Orderable key: larger logit first, then lower index; NaN ranks as -inf and
+// -0 as +0.  Zero is below every real key.
+__device__ __forceinline__ uint64_t route_key(float l, int e)
+{
+    uint32_t u = __float_as_uint(l);
+    if (l != l) u = 0xFF800000u;
+    if (l == 0.0f) u = 0u;
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(v, off);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__global__ void __launch_bounds__(256) route_kernel(RouteParams p)
+{
+    __shared__ int slot_of[kMaxExperts];
+    __shared__ int cur_union[kMaxSlots];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+    const int m = p.m, k = p.k, E = p.E;
+    const int nj = (E + 63) >> 6;
+
+    // ---- top-k and weights, one token per wave ----
+    for (int t = w; t < m; t += nw) {
+        uint64_t key[kMaxExperts / 64];
+#pragma unroll
+        for (int j = 0; j < kMaxExperts / 64; ++j) {
+            const int e = lane + 64 * j;
+            key[j] = (j < nj && e < E) ? route_key(p.logits[(size_t)t * E + e], e) : 0ull;
+        }
+        int my_e = -1;
+        for (int r = 0; r < k; ++r) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < kMaxExperts / 64; ++j) best = key[j] > best ? key[j] : best;
+            best = wave_max_u64(best);
+#pragma unroll
+            for (int j = 0; j < kMaxExperts / 64; ++j)
+                if (key[j] == best) key[j] = 0ull;
+            if (lane == r) my_e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        }
+        double lr = -INFINITY;
+        if (lane < k) {
+            const float l = p.logits[(size_t)t * E + my_e];
+            lr = (l != l) ? -INFINITY : (double)l;
+        }
+        const double l0 = __shfl(lr, 0);
+        const double ex = (lane < k) ? ((lr == l0) ? 1.0 : exp(lr - l0)) : 0.0;
+        double sum = 0.0;
+        for (int r = 0; r < k; ++r) sum += __shfl(ex, r);
+        if (lane < k) {
+            const double sc = p.scale ? (double)p.scale[my_e] : 1.0;
+            p.ids[(size_t)t * k + lane] = my_e;
+            p.w[(size_t)t * k + lane] = (float)(ex / sum * sc);
+        }
+    }
+
+    // ---- plan: unused entries are -1 ----
+    const int total = 2 * m + 4 + 4 * m * k;
+    for (int i = tid; i < total; i += blockDim.x) p.plan[i] = -1;
+    for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
+    __syncthreads();
+    if (w != 0) return;
+
+    int32_t* sub_tok = p.plan + 1;
+    int32_t* sub_uni = p.plan + (m + 2);
+    int32_t* uexp = p.plan + (2 * m + 3);
+    int32_t* pslot = p.plan + (2 * m + 3 + m * k);
+    int32_t* spb = p.plan + (2 * m + 3 + 2 * m * k);
+    int32_t* sp = p.plan + (2 * m + 4 + 3 * m * k);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    int S = 0, base = 0, usize = 0, s_tok = 0, pos = 0;
+    if (lane == 0) {
+        sub_tok[0] = 0;
+        sub_uni[0] = 0;
+    }
+
+    // CSR of the sub-batch [t0, t1): pairs grouped by slot, ascending.
+    auto close_sub = [&](int t0, int t1) {
+        const int P0 = t0 * k, P1 = t1 * k;
+        int cnt = 0;   // lane j < usize: pairs in slot j
+        for (int c = P0; c < P1; c += 64) {
+            const int pp = c + lane;
+            const int sl = (pp < P1) ? slot_of[p.ids[pp]] : -1;
+            for (int j = 0; j < usize; ++j) {
+                const uint64_t msk = __ballot(sl == j);
+                if (lane == j) cnt += __popcll(msk);
+            }
+        }
+        int excl = cnt;   // exclusive prefix over lanes 0..usize-1
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(excl, off);
+            if (lane >= off) excl += o;
+        }
+        excl -= cnt;
+        int cur = pos + excl;
+        if (lane < usize) spb[base + lane] = cur;
+        for (int c = P0; c < P1; c += 64) {
+            const int pp = c + lane;
+            const int sl = (pp < P1) ? slot_of[p.ids[pp]] : -1;
+            for (int j = 0; j < usize; ++j) {
+                const uint64_t msk = __ballot(sl == j);
+                const int start = __shfl(cur, j);
+                if (sl == j) sp[start + __popcll(msk & lt)] = pp;
+                if (lane == j) cur += __popcll(msk);
+            }
+        }
+        pos += P1 - P0;
+        __builtin_amdgcn_wave_barrier();
+        if (lane < usize) slot_of[cur_union[lane]] = -1;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    for (int t = 0; t < m; ++t) {
+        const int e = (lane < k) ? p.ids[(size_t)t * k + lane] : 0;
+        int cur = (lane < k) ? slot_of[e] : 0;
+        bool fresh = (lane < k) && cur < 0;
+        uint64_t fm = __ballot(fresh);
+        int nf = __popcll(fm);
+        if (usize + nf > p.cap) {
+            close_sub(s_tok, t);
+            ++S;
+            if (lane == 0) {
+                sub_tok[S] = t;
+                sub_uni[S] = base + usize;
+            }
+            base += usize;
+            usize = 0;
+            s_tok = t;
+            fresh = (lane < k);
+            fm = __ballot(fresh);
+            nf = __popcll(fm);
+        }
+        if (fresh) {
+            cur = usize + __popcll(fm & lt);
+            slot_of[e] = cur;
+            cur_union[cur] = e;
+            uexp[base + cur] = e;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (lane < k) pslot[(size_t)t * k + lane] = cur;
+        usize += nf;
+    }
+    close_sub(s_tok, m);
+    ++S;
+    if (lane == 0) {
+        sub_tok[S] = m;
+        sub_uni[S] = base + usize;
+        spb[base + usize] = m * k;
+        p.plan[0] = S;
+    }
+}
+
+}  // namespace ffnq

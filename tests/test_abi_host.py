@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point include/ffnq.h declares, and refuses bad arguments with the documented
+status codes before touching the GPU.  No compute call is made."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import moe_expert_dequant_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# fake, 16-byte aligned "device" addresses: every call below is refused (or is a
+# workspace query / m == 0 no-op) before any pointer is dereferenced
+A = 0x10000
+
+
+def addr(i):
+    return A * (i + 1)
+
+
+def header_decls():
+    with open(os.path.join(ROOT, "include", "ffnq.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"FFNQ_API\s+[\w\s\*]+?\b(ffnq_\w+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    names = header_decls()
+    assert set(names) == set(fq.EXPORTS)
+    L = fq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = fq.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.ffnq_status_string(code)
+
+
+def mat(fmt, n, k, base):
+    return fq.QMat(fmt, n, k, addr(base), addr(base + 1), addr(base + 2) if fmt == fq.FMT_INT4_AFFINE_G64 else None)
+
+
+def ffn(fmt_gu, fmt_d, hidden, inter):
+    return fq.Ffn(mat(fmt_gu, inter, hidden, 0), mat(fmt_gu, inter, hidden, 10), mat(fmt_d, hidden, inter, 20))
+
+
+def call_dense(f, hidden=256, inter=512, m=2, act=fq.ACT_SILU, tail=fq.TAIL_RESIDUAL, x=addr(40), out=addr(50),
+               norm=addr(60), eps=1e-6, ws=None, ws_bytes=None, shared=False):
+    L = fq.lib()
+    size = C.c_size_t(ws_bytes or 0)
+    fn = L.ffnq_shared_expert if shared else L.ffnq_dense
+    rc = fn(C.byref(f) if f is not None else None, hidden, inter, m, act, tail, x, out, norm, eps, ws,
+            C.byref(size), None)
+    return rc, size.value
+
+
+I8, I4 = fq.FMT_INT8_ROW, fq.FMT_INT4_AFFINE_G64
+
+
+def test_dense_workspace_query_and_noop():
+    f = ffn(I4, I4, 256, 512)
+    rc, n = call_dense(f)
+    assert rc == 0 and n > 0
+    rc, n0 = call_dense(f, m=0)
+    assert rc == 0 and n0 == 0
+    # m == 0 with a (fake) workspace: a no-op
+    rc, _ = call_dense(f, m=0, ws=addr(70), ws_bytes=0)
+    assert rc == 0
+    # too small a workspace
+    rc, _ = call_dense(f, ws=addr(70), ws_bytes=n - 1)
+    assert rc == -4
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(hidden=0), -1), (dict(inter=0), -1), (dict(m=-1), -1),
+    (dict(x=None), -1), (dict(out=None), -1),
+    (dict(x=addr(40) + 8), -1),                   # misaligned
+    (dict(out=addr(40) + 256), -1),               # overlaps x
+    (dict(act=7), -2), (dict(tail=fq.TAIL_SIGMOID_GATE), -2), (dict(tail=9), -2),
+    (dict(tail=fq.TAIL_RMSNORM, norm=None), -1),
+    (dict(tail=fq.TAIL_RMSNORM, eps=-1.0), -1),
+    (dict(tail=fq.TAIL_RMSNORM, eps=float("nan")), -1),
+])
+def test_dense_refusals(case, expect):
+    f = ffn(I8, I4, 256, 512)
+    rc, _ = call_dense(f, **case)
+    assert rc == expect
+
+
+def test_dense_shape_and_format_refusals():
+    assert call_dense(None)[0] == -1
+    bad = ffn(I4, I4, 256, 512)
+    bad.down.n = 128                                     # down rows != hidden
+    assert call_dense(bad)[0] == -1
+    bad = ffn(I4, I4, 256, 512)
+    bad.gate.k = 200                                     # k not a multiple of 64
+    assert call_dense(bad)[0] == -1
+    bad = ffn(I4, I4, 192, 512)                          # INT4 k % 128 == 64
+    assert call_dense(bad, hidden=192)[0] == -2
+    bad = ffn(I4, I4, 256, 512)
+    bad.up.fmt = I8                                      # gate/up formats differ
+    assert call_dense(bad)[0] == -2
+    bad = ffn(I4, I4, 256, 512)
+    bad.gate.fmt = 5                                     # unknown format
+    assert call_dense(bad)[0] == -2
+    bad = ffn(I4, I4, 256, 512)
+    bad.gate.z = None                                    # INT4 without zero points
+    assert call_dense(bad)[0] == -1
+    bad = ffn(I4, I4, 256, 512)
+    bad.down.q = addr(20) + 4                            # misaligned weights
+    assert call_dense(bad)[0] == -1
+
+
+def test_shared_expert_tails():
+    f = ffn(I8, I8, 256, 704)
+    for tail in (fq.TAIL_NONE, fq.TAIL_RMSNORM, fq.TAIL_SIGMOID_GATE):
+        rc, n = call_dense(f, inter=704, tail=tail, shared=True)
+        assert rc == 0 and n > 0
+    assert call_dense(f, inter=704, tail=fq.TAIL_RESIDUAL, shared=True)[0] == -2
+    assert call_dense(f, inter=704, tail=fq.TAIL_SIGMOID_GATE, norm=None, shared=True)[0] == -1
+
+
+def call_route(m=4, E=16, k=4, cap=8, plan_bytes=None, logits=addr(1), ids=addr(2), w=addr(3), plan=addr(4),
+               scale=None):
+    L = fq.lib()
+    pb = 4 * fq.plan_ints(m, k) if plan_bytes is None else plan_bytes
+    return L.ffnq_moe_route(logits, scale, m, E, k, cap, ids, w, plan, pb, None)
+
+
+def test_route_refusals():
+    assert call_route(m=0) == 0                               # no-op
+    assert call_route(k=0) == -1
+    assert call_route(k=17) == -1
+    assert call_route(E=0) == -1
+    assert call_route(m=-1) == -1
+    assert call_route(logits=None) == -1
+    assert call_route(plan=addr(4) + 4) == -1
+    assert call_route(E=2048, k=4) == -2                      # more experts than the router holds
+    assert call_route(cap=33) == -2                           # above the 32-slot ceiling
+    assert call_route(k=4, cap=3) == -3                       # not even one token fits
+    assert call_route(plan_bytes=4 * fq.plan_ints(4, 4) - 4) == -4
+
+
+def call_routed(f, E=8, hidden=256, inter=256, m=3, k=2, act=fq.ACT_SILU, x=addr(40), ids=addr(41), w=addr(42),
+                plan=addr(43), seed=addr(44), resid=addr(50), ws=None, ws_bytes=0):
+    L = fq.lib()
+    size = C.c_size_t(ws_bytes)
+    rc = L.ffnq_moe_routed_batched(C.byref(f), E, hidden, inter, m, k, act, x, ids, w, plan, seed, resid, ws,
+                                   C.byref(size), None)
+    return rc, size.value
+
+
+def test_routed_refusals_and_query():
+    f = ffn(I4, I4, 256, 256)
+    rc, n = call_routed(f)
+    assert rc == 0 and n > 0
+    assert call_routed(f, seed=None)[0] == 0
+    assert call_routed(f, m=0)[0] == 0 and call_routed(f, m=0)[1] == 0
+    assert call_routed(ffn(I8, I4, 256, 256))[0] == -2        # routed experts must be INT4-affine
+    assert call_routed(ffn(I4, I8, 256, 256))[0] == -2
+    assert call_routed(f, k=9)[0] == -1
+    assert call_routed(f, act=3)[0] == -2
+    assert call_routed(f, plan=None)[0] == -1
+    assert call_routed(f, resid=addr(40) + 64)[0] == -1       # overlaps x
+    assert call_routed(f, ws=addr(60), ws_bytes=n - 256)[0] == -4
