@@ -106,6 +106,7 @@ def main():
     ap.add_argument("--m", type=int, default=1, help="tokens per call for the headline value")
     ap.add_argument("--copies", type=int, default=8, help="distinct weight copies rotated over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single", action="store_true", help="time only --m (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is a "
@@ -118,7 +119,7 @@ def main():
         sys.exit(2)
 
     res = {}
-    for m in sorted({args.m, 1, 4}):
+    for m in ([args.m] if args.single else sorted({args.m, 1, 4})):
         wall, per_call, nbytes = run_gpu(m, args.steps, args.warmup, args.copies)
         avg = float(np.mean(per_call)) * 1e-3
         res[m] = dict(wall=wall, avg_s=avg, med_s=float(np.median(per_call)) * 1e-3, bytes=nbytes,

@@ -31,13 +31,15 @@ __device__ __forceinline__ float bf16_f32(uint16_t b) { return __uint_as_float((
 // 128 + code.  0x4300 is bf16 128.0 with a mantissa step of 1, so OR-ing a
 // code into its low bits is exact.  Register v holds codes (v, v+4), so the
 // element order is the permutation [0,4,1,5,2,6,3,7] of the eight inputs.
+// Each register is one v_bitop3_b32 ((a & b) | c, truth table 0xEA) after a
+// shift.
 __device__ __forceinline__ u32x4 unpack_int4_biased(uint32_t w)
 {
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x43004300u, (unsigned char)0xEA);
+    r[1] = __builtin_amdgcn_bitop3_b32(w >> 4, 0x000F000Fu, 0x43004300u, (unsigned char)0xEA);
+    r[2] = __builtin_amdgcn_bitop3_b32(w >> 8, 0x000F000Fu, 0x43004300u, (unsigned char)0xEA);
+    r[3] = __builtin_amdgcn_bitop3_b32(w >> 12, 0x000F000Fu, 0x43004300u, (unsigned char)0xEA);
     return r;
 }
 
@@ -111,6 +113,46 @@ __device__ __forceinline__ double act_f64(int act, double g)
     if (act == 1) return g / (1.0 + exp(-g));
     const double c = 0.7978845608028654;   // sqrt(2/pi)
     return 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g)));
+}
+
+
+// Direct global->LDS loads (gfx950 global_load_lds_dword / _dwordx4): lane i
+// writes its 4 or 16 bytes to LDS byte address lds + i*size.  Issued from
+// inline asm so that the compiler's counter bookkeeping covers only the
+// loads it sees; the caller waits for these with an explicit
+// s_waitcnt vmcnt(N) (loads retire in order) before a barrier.  M0 carries
+// the LDS base and is restored afterwards; the base must be wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "memory");
 }
 
 }  // namespace ffnq

@@ -19,9 +19,7 @@ namespace {
 
 using namespace ffnq;
 
-constexpr int kKGMax = 16;            // largest K split of the down kernel
-constexpr size_t kLdsBudget = 64 * 1024;
-constexpr int kDownWaves = 4;         // row tiles per down workgroup
+constexpr size_t kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -34,6 +32,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
 }
 
 int block_k(int fmt) { return fmt == FFNQ_FMT_INT4_AFFINE_G64 ? 128 : 64; }
+
+// library format code -> kernel format code
+int to_fmt(int f) { return f == FFNQ_FMT_INT4_AFFINE_G64 ? ffnq::FMT_INT4 : ffnq::FMT_INT8; }
+int to_fmt_dev(int f) { return to_fmt(f); }
 
 // Compute units of the current device, cached per device ordinal.
 int device_cus()
@@ -107,67 +109,69 @@ MatDev mat_dev(const ffnq_qmat& w)
 // ---------------------------------------------------------------------------
 // launch configuration
 
-struct GUConfig {
-    int nt, mt, ks, rows_cap;
+constexpr int kRefCUs = 256;       // K-split heuristic reference (keeps workspace sizes device-independent)
+constexpr int kKSMax = 8;          // waves per workgroup (upper bound used for LDS sizing)
+
+struct KConfig {
+    int nt, mt, ks, rows_cap, kg;
     size_t lds;
 };
 
-GUConfig gu_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+KConfig gu_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
 {
-    GUConfig c;
+    KConfig c{};
+    const int NB = K / block_k(fmt);
     const int rp = std::max(1, std::min(rows_total, 32));
     c.nt = rp <= 16 ? 1 : 2;
     c.mt = c.nt == 2 ? 4 : (rp <= 1 ? 1 : (rp <= 2 ? 2 : 4));
-    const int NB = K / block_k(fmt);
+    c.rows_cap = std::min(rp, 16 * c.nt);
+    c.kg = 1;
+    const long long tiles = (N + 15) / 16;
     const long long target = (long long)cus * 12;
     int ks = 1;
-    while (ks < 8 && items_est * ks * 2 <= target && ks * 2 <= NB) ks *= 2;
+    while (ks < kKSMax && items_est * tiles * ks * 2 <= target && ks * 2 <= NB) ks *= 2;
     c.ks = ks;
-    const size_t per = (size_t)(fmt == FFNQ_FMT_INT8_ROW ? 3 : 2) * c.nt * 4;
-    const size_t red = (size_t)ks * per * 64 * sizeof(float);
-    const size_t row_bytes = (size_t)(K + 8) * 2;
-    int cap = std::min(rp, 16 * c.nt);
-    while (cap > 1 && red + cap * row_bytes > kLdsBudget) --cap;
-    c.rows_cap = cap;
-    c.lds = red + cap * row_bytes;
-    (void)N;
+    for (;;) {
+        c.lds = lds_layout(2, to_fmt_dev(fmt), NB, c.rows_cap, c.ks, 2 * c.nt * 4).total;
+        if (c.lds <= kLdsBudget || c.rows_cap <= 1) break;
+        --c.rows_cap;
+    }
     return c;
 }
 
-struct DownConfig {
-    int nt, mt, kg, rows_cap;
-    size_t lds;
-};
-
-DownConfig down_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+// K ranges of the down projection: enough for the activation slice of a
+// range to fit LDS, and enough workgroups when the matrix has few row tiles.
+int down_kg(int fmt, int K, int N, int rows_total)
 {
-    DownConfig c;
+    const int NB = K / block_k(fmt);
+    const int r2 = 2 * std::max(1, rows_total);
+    const int nt = std::min(r2, 64) <= 16 ? 1 : (std::min(r2, 64) <= 32 ? 2 : 4);
+    const int rows_cap = std::min(std::min(r2, 64), 16 * nt);
+    const long long tiles = (N + 15) / 16;
+    int kg = (int)std::max<long long>(1, (kRefCUs + tiles - 1) / tiles);
+    kg = std::min(kg, NB);
+    while (kg < NB && lds_layout(1, to_fmt_dev(fmt), (NB + kg - 1) / kg, rows_cap, kKSMax, 2 * nt).total > kLdsBudget)
+        ++kg;
+    return kg;
+}
+
+KConfig down_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+{
+    KConfig c{};
+    const int NB = K / block_k(fmt);
     const int r2 = 2 * std::max(1, rows_total);
     const int rp = std::min(r2, 64);
     c.nt = rp <= 16 ? 1 : (rp <= 32 ? 2 : 4);
     c.mt = c.nt > 1 ? 4 : (rp <= 2 ? 2 : 4);
-    const int BK = block_k(fmt);
-    const int NB = K / BK;
-    const long long target = (long long)cus * 16;
-    int kg = 1;
-    while (kg < kKGMax && kg < NB && items_est * kDownWaves * kg < target) ++kg;
-    c.rows_cap = std::min(r2, 16 * c.nt);
-    for (;;) {
-        const int nbl = (NB + kg - 1) / kg;
-        const size_t xb = (size_t)c.rows_cap * (nbl * BK + 8) * 2;
-        const size_t resb = kg == 1 ? (size_t)r2 * 16 * kDownWaves * sizeof(float) : 0;
-        c.lds = xb + resb;
-        if (c.lds <= kLdsBudget) break;
-        if (kg < std::min(kKGMax, NB)) {
-            ++kg;
-        } else if (c.rows_cap > 1) {
-            --c.rows_cap;
-        } else {
-            break;
-        }
-    }
-    c.kg = kg;
-    (void)N;
+    c.rows_cap = std::min(rp, 16 * c.nt);
+    c.kg = down_kg(fmt, K, N, rows_total);
+    const int nbk = (NB + c.kg - 1) / c.kg;
+    const long long tiles = (N + 15) / 16;
+    const long long target = (long long)cus * 12;
+    int ks = 1;
+    while (ks < kKSMax && items_est * tiles * c.kg * ks * 2 <= target && ks * 2 <= nbk) ks *= 2;
+    c.ks = ks;
+    c.lds = lds_layout(1, to_fmt_dev(fmt), nbk, c.rows_cap, c.ks, 2 * c.nt).total;
     return c;
 }
 
@@ -180,8 +184,10 @@ DownConfig down_config(int fmt, int K, int N, long long items_est, int rows_tota
         return true;                                                                           \
     }
 
-bool launch_gu(int fmt, const GUConfig& c, dim3 grid, dim3 block, hipStream_t stream, const GUParams& prm)
+bool launch_gu(int fmt, const KConfig& c, long long items, int N, hipStream_t stream, const GUParams& prm)
 {
+    const long long tiles = (N + 15) / 16;
+    const dim3 grid((unsigned)std::min<long long>(items * tiles, 65535)), block(64 * c.ks);
     FFNQ_GU_CASE(FMT_INT4, 1, 1) FFNQ_GU_CASE(FMT_INT4, 1, 2) FFNQ_GU_CASE(FMT_INT4, 1, 4)
     FFNQ_GU_CASE(FMT_INT4, 2, 4) FFNQ_GU_CASE(FMT_INT8, 1, 1) FFNQ_GU_CASE(FMT_INT8, 1, 2)
     FFNQ_GU_CASE(FMT_INT8, 1, 4) FFNQ_GU_CASE(FMT_INT8, 2, 4)
@@ -194,34 +200,30 @@ bool launch_gu(int fmt, const GUConfig& c, dim3 grid, dim3 block, hipStream_t st
         return true;                                                                           \
     }
 
-bool launch_down(int fmt, const DownConfig& c, dim3 grid, dim3 block, hipStream_t stream, const DownParams& prm)
+bool launch_down(int fmt, const KConfig& c, long long items, int N, hipStream_t stream, const DownParams& prm)
 {
+    const long long tiles = (N + 15) / 16;
+    const dim3 grid((unsigned)std::min<long long>(items * tiles, 65535), c.kg), block(64 * c.ks);
     FFNQ_DOWN_CASE(FMT_INT4, 1, 2) FFNQ_DOWN_CASE(FMT_INT4, 1, 4) FFNQ_DOWN_CASE(FMT_INT4, 2, 4)
     FFNQ_DOWN_CASE(FMT_INT4, 4, 4) FFNQ_DOWN_CASE(FMT_INT8, 1, 2) FFNQ_DOWN_CASE(FMT_INT8, 1, 4)
     FFNQ_DOWN_CASE(FMT_INT8, 2, 4) FFNQ_DOWN_CASE(FMT_INT8, 4, 4)
     return false;
 }
 
-int to_fmt(int f) { return f == FFNQ_FMT_INT4_AFFINE_G64 ? FMT_INT4 : FMT_INT8; }
-
 // ---------------------------------------------------------------------------
 // dense FFN (ffnq_dense and ffnq_shared_expert)
 
 struct DenseWs {
-    size_t act_hi, act_lo, partial, counters, hbuf, logit, total;
+    size_t act, part, logit, total;
 };
 
-DenseWs dense_ws(int hidden, int inter, int m)
+DenseWs dense_ws(int fmt_down, int hidden, int inter, int m)
 {
     DenseWs w{};
     size_t o = 0;
-    const size_t plane = align_up((size_t)m * inter * 2, 256);
-    w.act_hi = o; o += plane;
-    w.act_lo = o; o += plane;
-    w.partial = o; o += align_up((size_t)kKGMax * 2 * m * hidden * sizeof(float), 256);
-    const int groups = (hidden + 16 * kDownWaves - 1) / (16 * kDownWaves);
-    w.counters = o; o += align_up((size_t)groups * sizeof(unsigned), 256);
-    w.hbuf = o; o += align_up((size_t)m * hidden * sizeof(float), 256);
+    const int kg = down_kg(fmt_down, inter, hidden, m);
+    w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
+    w.part = o; o += align_up((size_t)kg * m * hidden * sizeof(float), 256);
     w.logit = o; o += align_up((size_t)m * sizeof(float), 256);
     w.total = m == 0 ? 0 : o;
     return w;
@@ -232,12 +234,10 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
 {
     const int cus = device_cus();
     unsigned char* base = static_cast<unsigned char*>(ws);
-    const DenseWs L = dense_ws(hidden, inter, m);
+    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m);
     const int gfmt = to_fmt(ffn->gate.fmt), dfmt = to_fmt(ffn->down.fmt);
-    const int groups = (hidden + 16 * kDownWaves - 1) / (16 * kDownWaves);
 
-    const int tiles = (inter + 15) / 16;
-    const GUConfig gc = gu_config(ffn->gate.fmt, hidden, inter, tiles, m, cus);
+    const KConfig gc = gu_config(ffn->gate.fmt, hidden, inter, 1, m, cus);
     GUParams gp{};
     gp.gate = mat_dev(ffn->gate);
     gp.up = mat_dev(ffn->up);
@@ -249,33 +249,28 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
     gp.m = m;
     gp.rows_cap = gc.rows_cap;
     gp.plan = nullptr;
-    gp.act_hi = reinterpret_cast<uint16_t*>(base + L.act_hi);
-    gp.act_lo = reinterpret_cast<uint16_t*>(base + L.act_lo);
+    gp.act_out = reinterpret_cast<uint16_t*>(base + L.act);
     gp.act_rows = m;
     if (tail == FFNQ_TAIL_SIGMOID_GATE) {
         gp.gate_vec = aux;
         gp.logit = reinterpret_cast<float*>(base + L.logit);
     }
-    gp.zero_ptr = reinterpret_cast<unsigned*>(base + L.counters);
-    gp.zero_count = groups;
-    if (!launch_gu(gfmt, gc, dim3(tiles), dim3(64 * gc.ks), stream, gp)) return FFNQ_ERR_UNSUPPORTED;
+    if (!launch_gu(gfmt, gc, 1, inter, stream, gp)) return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    const DownConfig dc = down_config(ffn->down.fmt, inter, hidden, groups, m, cus);
+    const KConfig dc = down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
     DownParams dp{};
     dp.down = mat_dev(ffn->down);
     dp.N = hidden;
     dp.K = inter;
-    dp.act_hi = gp.act_hi;
-    dp.act_lo = gp.act_lo;
+    dp.act = gp.act_out;
     dp.act_rows = m;
     dp.m = m;
     dp.rows_cap = dc.rows_cap;
+    dp.KG = dc.kg;
     dp.plan = nullptr;
-    dp.partial = reinterpret_cast<float*>(base + L.partial);
-    dp.counters = reinterpret_cast<unsigned*>(base + L.counters);
     dp.out = out;
-    dp.hbuf = reinterpret_cast<float*>(base + L.hbuf);
+    dp.part = reinterpret_cast<float*>(base + L.part);
     dp.logit = reinterpret_cast<const float*>(base + L.logit);
     switch (tail) {
         case FFNQ_TAIL_RESIDUAL: dp.tail = TAIL_RESIDUAL; break;
@@ -283,11 +278,17 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
         case FFNQ_TAIL_SIGMOID_GATE: dp.tail = TAIL_SIGMOID; break;
         default: dp.tail = TAIL_NONE; break;
     }
-    if (!launch_down(dfmt, dc, dim3(groups, dc.kg), dim3(64 * kDownWaves), stream, dp)) return FFNQ_ERR_UNSUPPORTED;
+    if (!launch_down(dfmt, dc, 1, hidden, stream, dp)) return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     if (tail == FFNQ_TAIL_RMSNORM) {
-        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), 0, stream, dp.hbuf, aux, out, hidden, eps);
+        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), 0, stream, dp.part, dc.kg, m, aux, out, hidden, eps);
+        if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    } else if (dc.kg > 1) {
+        const long long total = (long long)m * hidden;
+        const int grid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
+        hipLaunchKernelGGL(ksum_tail_kernel, dim3(grid), dim3(256), 0, stream, dp.part, dc.kg, m, hidden, dp.tail, out,
+                           dp.logit);
         if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
     }
     return FFNQ_OK;
@@ -316,7 +317,7 @@ int dense_common(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int
         if (!aux || misaligned(aux)) return FFNQ_ERR_INVALID;
     }
     if (tail == FFNQ_TAIL_RMSNORM && !(eps >= 0.0f && std::isfinite(eps))) return FFNQ_ERR_INVALID;
-    const DenseWs L = dense_ws(hidden, inter, m);
+    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m);
     if (!ws) {
         *ws_bytes = L.total;
         return FFNQ_OK;
@@ -331,21 +332,17 @@ int dense_common(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int
 // routed half
 
 struct RoutedWs {
-    size_t act_hi, act_lo, partial, counters, pair_out, total;
+    size_t act, part, total;
 };
 
 RoutedWs routed_ws(int hidden, int moe_inter, int m, int k)
 {
     RoutedWs w{};
     const size_t P = (size_t)m * k;
+    const int kg = down_kg(FFNQ_FMT_INT4_AFFINE_G64, moe_inter, hidden, m);
     size_t o = 0;
-    const size_t plane = align_up(P * moe_inter * 2, 256);
-    w.act_hi = o; o += plane;
-    w.act_lo = o; o += plane;
-    w.partial = o; o += align_up((size_t)kKGMax * 2 * P * hidden * sizeof(float), 256);
-    const int groups = (hidden + 16 * kDownWaves - 1) / (16 * kDownWaves);
-    w.counters = o; o += align_up(P * groups * sizeof(unsigned), 256);
-    w.pair_out = o; o += align_up(P * hidden * sizeof(float), 256);
+    w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
+    w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
     w.total = m == 0 ? 0 : o;
     return w;
 }
@@ -432,11 +429,9 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     unsigned char* base = static_cast<unsigned char*>(ws);
     const int P = m * top_k;
     const long long u_est = std::min<long long>(P, n_experts);
-    const int groups = (hidden + 16 * kDownWaves - 1) / (16 * kDownWaves);
-    const int tiles = (moe_inter + 15) / 16;
 
     // phase 1: gate/up + activation per union entry and tile
-    const GUConfig gc = gu_config(FFNQ_FMT_INT4_AFFINE_G64, hidden, moe_inter, u_est * tiles, m, cus);
+    const KConfig gc = gu_config(FFNQ_FMT_INT4_AFFINE_G64, hidden, moe_inter, u_est, m, cus);
     GUParams gp{};
     gp.gate = mat_dev(experts->gate);
     gp.up = mat_dev(experts->up);
@@ -451,45 +446,36 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     gp.top_k = top_k;
     gp.topk_ids = topk_ids;
     gp.n_experts = n_experts;
-    gp.act_hi = reinterpret_cast<uint16_t*>(base + L.act_hi);
-    gp.act_lo = reinterpret_cast<uint16_t*>(base + L.act_lo);
+    gp.act_out = reinterpret_cast<uint16_t*>(base + L.act);
     gp.act_rows = P;
-    gp.zero_ptr = reinterpret_cast<unsigned*>(base + L.counters);
-    gp.zero_count = P * groups;
-    const long long gu_items = u_est * tiles;
-    const int gu_grid = (int)std::min<long long>(gu_items, 65535);
-    if (!launch_gu(FMT_INT4, gc, dim3(gu_grid), dim3(64 * gc.ks), stream, gp)) return FFNQ_ERR_UNSUPPORTED;
+    if (!launch_gu(FMT_INT4, gc, u_est, moe_inter, stream, gp)) return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    // phase 2: down per union entry and row group, d_p to pair_out
-    const DownConfig dc = down_config(FFNQ_FMT_INT4_AFFINE_G64, moe_inter, hidden, u_est * groups, m, cus);
+    // phase 2: down per union entry and tile, d_p to pair_out
+    const KConfig dc = down_config(FFNQ_FMT_INT4_AFFINE_G64, moe_inter, hidden, u_est, m, cus);
     DownParams dp{};
     dp.down = mat_dev(experts->down);
     dp.N = hidden;
     dp.K = moe_inter;
-    dp.act_hi = gp.act_hi;
-    dp.act_lo = gp.act_lo;
+    dp.act = gp.act_out;
     dp.act_rows = P;
     dp.m = m;
     dp.rows_cap = dc.rows_cap;
+    dp.KG = dc.kg;
     dp.plan = plan;
     dp.top_k = top_k;
     dp.topk_ids = topk_ids;
     dp.n_experts = n_experts;
-    dp.partial = reinterpret_cast<float*>(base + L.partial);
-    dp.counters = reinterpret_cast<unsigned*>(base + L.counters);
     dp.tail = TAIL_PAIR;
-    dp.hbuf = reinterpret_cast<float*>(base + L.pair_out);
-    const int dn_grid = (int)std::min<long long>(u_est * groups, 65535);
-    if (!launch_down(FMT_INT4, dc, dim3(dn_grid, dc.kg), dim3(64 * kDownWaves), stream, dp))
-        return FFNQ_ERR_UNSUPPORTED;
+    dp.part = reinterpret_cast<float*>(base + L.part);
+    if (!launch_down(FMT_INT4, dc, u_est, hidden, stream, dp)) return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     // seeded rank-ordered reduce + residual
     const long long total = (long long)m * hidden;
     const int rgrid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
-    hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.hbuf, topk_w, topk_ids, n_experts,
-                       seed, resid, m, top_k, hidden);
+    hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, dc.kg, topk_w, topk_ids,
+                       n_experts, seed, resid, m, top_k, hidden);
     return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
 }
 

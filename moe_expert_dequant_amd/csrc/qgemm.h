@@ -4,7 +4,7 @@
 // ([llama/dense.rs] gate/up/down GEMVs; [gemma4/shared_expert.rs] the
 // batched M-row GEMMs; [qwen/moe_batch.rs] the routed phase-1 and phase-2
 // dispatches).  A wave owns a 16-row tile of one (or two) weight matrices and
-// streams its packed codes from HBM with 16-byte loads, a few blocks ahead.
+// streams its packed codes from HBM with 16-byte loads, several blocks ahead.
 // Codes are widened in registers to bf16 "128 + code" (exact) and multiplied
 // on the MFMA unit (v_mfma_f32_16x16x32_bf16) against up to 16 activation
 // rows per token block; the code bias and the INT4 zero point are removed
@@ -12,8 +12,11 @@
 //     sum_k s (q - z) x_k = s * (sum_k (128 + q) x_k - (128 + z) sum_k x_k)
 // INT4 groups (64 inputs) are kept apart by a lane permutation
 // (v_permlane32_swap) so that each MFMA step sees one group only.
-// Activations are staged once per workgroup in LDS, already in the order the
-// MFMA consumes, so the weight stream is the only global traffic in the loop.
+//
+// Activations reach the MFMA in "consumption order" (see nat_run/cons_pos):
+// gate/up stage x in LDS in that order; the activation written by gate/up
+// for the down projection is already in that order, so the down kernel reads
+// it straight from L2 (decode sizes) or stages it in LDS (prefill sizes).
 #pragma once
 #include "device.h"
 
@@ -24,9 +27,9 @@ enum { FMT_INT8 = 1, FMT_INT4 = 2 };
 template <int FMT>
 struct FmtT;
 template <>
-struct FmtT<FMT_INT4> { static constexpr int BK = 128; };   // inputs per 64-byte block row
+struct FmtT<FMT_INT4> { static constexpr int BK = 128, STEPS = 4; };   // inputs per 64-byte block row
 template <>
-struct FmtT<FMT_INT8> { static constexpr int BK = 64; };
+struct FmtT<FMT_INT8> { static constexpr int BK = 64, STEPS = 2; };
 
 // A quantized matrix on the device (expert 0 of a stack for routed calls).
 struct MatDev {
@@ -37,6 +40,8 @@ struct MatDev {
     long long qe;   // bytes of codes per expert
     long long se;   // scale (and zero) elements per expert
 };
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // --------------------------------------------------------------------------
 // Consumption order.  Within a block of BK inputs, the wave reads the 16-byte
@@ -80,137 +85,308 @@ __device__ __forceinline__ int cons_index(int dfmt, int k)
 }
 
 // --------------------------------------------------------------------------
-// The streaming core.
+// The streaming engine.
+//
+// A workgroup owns one 16-row tile of NMAT weight matrices and a range of K
+// blocks; its KS waves split the range (wave ks takes local blocks ks,
+// ks+KS, ...).  The only global loads inside the K loop are the 16-byte code
+// loads, kept PF blocks ahead in a register ring.  Everything else comes from
+// LDS, staged once per item: the tile's INT4 scale/zero pairs and the
+// activation rows of the range (the host splits K across workgroups so that
+// they fit).  The ring is primed before the staging so that the first weight
+// loads overlap it.
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // two bf16 1.0
+constexpr int kSX = 8;                          // 16-byte activation pieces per thread per staging batch
+constexpr int kSZ = 4;                          // scale/zero pairs per thread and matrix per staging batch
+constexpr int kPfGU = 4;                        // code blocks in flight, gate/up kernel
+constexpr int kPfDN = 6;                        // code blocks in flight, down kernel
 
-template <int FMT, int NMAT, int NT, int MT>
-__device__ __forceinline__ void compute_block(const u32x4 (&cq)[NMAT], const uint32_t (&cs)[NMAT],
-                                              const uint32_t (&cz)[NMAT], const uint16_t* const (&xl)[NT],
-                                              int lb, f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT])
+template <int NMAT>
+struct TileW {
+    const uint8_t* q[NMAT];   // uniform: codes of row 0 of the tile, block kb0
+    uint32_t vq;              // lane: row offset + 16 * lane group
+};
+
+struct KRange {
+    int kb0, nbk;   // first block and number of blocks of the workgroup's K range
+    int KS, ks;     // waves splitting the range, this wave
+};
+
+// The waves of a workgroup split the range in pairs of consecutive blocks
+// (pair p goes to wave p % KS): a lane's 16-byte loads of blocks 2p and 2p+1
+// are the two halves of one 128-byte line of its row, so each line is fetched
+// by one wave in consecutive loads.  Returns the number of blocks of wave ks;
+// its q-th block is pair_block(ks, KS, q) and every such block is < nbk.
+__device__ __forceinline__ int pair_count(int nbk, int KS, int ks)
 {
-    constexpr int BK = FmtT<FMT>::BK;
+    const int np = (nbk + 1) >> 1;
+    if (ks >= np) return 0;
+    const int npw = (np - ks + KS - 1) / KS;
+    const bool odd_tail = (nbk & 1) && ((np - 1) % KS == ks);
+    return 2 * npw - (odd_tail ? 1 : 0);
+}
+__device__ __forceinline__ int pair_block(int ks, int KS, int q) { return 2 * (ks + (q >> 1) * KS) + (q & 1); }
+
+struct Lds {
+    uint8_t* x;             // activation slots [Rc][per_row] of 16 bytes, swizzled within each row
+    int per_row;            // 16-byte pieces per row (nbk * BK / 8)
+    int swz_mask, swz_shift;  // piece swizzle of row r: s(r) = (r >> swz_shift) & swz_mask
+    uint8_t* sz;            // INT4 scale/zero dword pairs [NMAT][16][zstride] (8 bytes each)
+    int zstride;            // odd, >= nbk
+    const long long* roff;  // element offset of each staged activation row in its source array
+};
+
+// Piece swizzle: piece j of row r sits at slot r*per_row + (j ^ s(r)).  For
+// INT4 (16 pieces per block) s(r) = r & 15 puts the 16 rows read by one
+// ds_read_b128 on 16 distinct bank groups; INT8 keeps the swizzle inside its
+// 8-piece blocks.
+template <int FMT>
+__device__ __forceinline__ void set_swizzle(Lds& L)
+{
+    if constexpr (FMT == FMT_INT4) {
+        L.swz_mask = 15;
+        L.swz_shift = 0;
+    } else {
+        L.swz_mask = 7;
+        L.swz_shift = (L.per_row & 15) ? 1 : 0;
+    }
+}
+
+
+// One K block of the tile: the codes cq of NMAT matrices (this lane's 16
+// bytes each) against NT token blocks of activations, read per token block
+// by xl(tb, xs) so that only one block's activations are live at a time.
+template <int FMT, int NMAT, int NT, int MT, typename XLoad>
+__device__ __forceinline__ void compute_block(const u32x4 (&cq)[NMAT], const uint32_t (&cs)[NMAT],
+                                              const uint32_t (&cz)[NMAT], XLoad&& xl, f32x4 (&tot)[NMAT][NT],
+                                              f32x4 (&one)[NT])
+{
     constexpr int MTC = (NT == 1) ? MT : 4;
+    constexpr int STEPS = FmtT<FMT>::STEPS;
     const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FMT == FMT_INT4) {
-        u32x4 xs[NT][4];
-#pragma unroll
-        for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) xs[tb][d] = *(const u32x4*)(xl[tb] + lb * BK + d * 32);
-        u32x4 c[NMAT];
+        u32x4 bw[NMAT][4];
+        float sg[NMAT][2], zg[NMAT][2];
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt) {
             // lanes 0-31 hold inputs [0,64) of the block, lanes 32-63 [64,128):
             // swap so that steps 0,1 hold group 0 and steps 2,3 group 1
             auto a = __builtin_amdgcn_permlane32_swap(cq[mt][0], cq[mt][2], false, false);
             auto b = __builtin_amdgcn_permlane32_swap(cq[mt][1], cq[mt][3], false, false);
-            c[mt][0] = a[0];
-            c[mt][2] = a[1];
-            c[mt][1] = b[0];
-            c[mt][3] = b[1];
+            bw[mt][0] = unpack_int4_biased(a[0]);
+            bw[mt][1] = unpack_int4_biased(b[0]);
+            bw[mt][2] = unpack_int4_biased(a[1]);
+            bw[mt][3] = unpack_int4_biased(b[1]);
+            sg[mt][0] = bf16lo_f32(cs[mt]);
+            sg[mt][1] = bf16hi_f32(cs[mt]);
+            zg[mt][0] = bf16lo_f32(cz[mt]) + 128.0f;
+            zg[mt][1] = bf16hi_f32(cz[mt]) + 128.0f;
         }
 #pragma unroll
-        for (int jg = 0; jg < 2; ++jg) {
-            f32x4 o[NT];
+        for (int tb = 0; tb < NT; ++tb) {
+            u32x4 xs[STEPS];
+            xl(tb, xs);
 #pragma unroll
-            for (int tb = 0; tb < NT; ++tb) {
-                o[tb] = mfma_bf16(xs[tb][2 * jg], ones, zero);
-                o[tb] = mfma_bf16(xs[tb][2 * jg + 1], ones, o[tb]);
-            }
+            for (int jg = 0; jg < 2; ++jg) {
+                f32x4 o = mfma_bf16(xs[2 * jg], ones, zero);
+                o = mfma_bf16(xs[2 * jg + 1], ones, o);
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                const u32x4 b0 = unpack_int4_biased(c[mt][2 * jg]);
-                const u32x4 b1 = unpack_int4_biased(c[mt][2 * jg + 1]);
-                const float s = jg ? bf16hi_f32(cs[mt]) : bf16lo_f32(cs[mt]);
-                const float zb = (jg ? bf16hi_f32(cz[mt]) : bf16lo_f32(cz[mt])) + 128.0f;
+                for (int mt = 0; mt < NMAT; ++mt) {
+                    f32x4 a = mfma_bf16(xs[2 * jg], bw[mt][2 * jg], zero);
+                    a = mfma_bf16(xs[2 * jg + 1], bw[mt][2 * jg + 1], a);
 #pragma unroll
-                for (int tb = 0; tb < NT; ++tb) {
-                    f32x4 a = mfma_bf16(xs[tb][2 * jg], b0, zero);
-                    a = mfma_bf16(xs[tb][2 * jg + 1], b1, a);
-#pragma unroll
-                    for (int i = 0; i < MTC; ++i) tot[mt][tb][i] = fmaf(s, fmaf(-zb, o[tb][i], a[i]), tot[mt][tb][i]);
+                    for (int i = 0; i < MTC; ++i)
+                        tot[mt][tb][i] = fmaf(sg[mt][jg], fmaf(-zg[mt][jg], o[i], a[i]), tot[mt][tb][i]);
                 }
             }
         }
     } else {
+        u32x4 bw[NMAT][2];
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            u32x4 xs[NT];
+        for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-            for (int tb = 0; tb < NT; ++tb) {
-                xs[tb] = *(const u32x4*)(xl[tb] + lb * BK + d * 32);
-                one[tb] = mfma_bf16(xs[tb], ones, one[tb]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
+            for (int d = 0; d < 2; ++d) {
                 const u32x2 p0 = unpack_int8_biased(cq[mt][2 * d]);
                 const u32x2 p1 = unpack_int8_biased(cq[mt][2 * d + 1]);
-                const u32x4 b = {p0[0], p0[1], p1[0], p1[1]};
+                bw[mt][d] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+            }
 #pragma unroll
-                for (int tb = 0; tb < NT; ++tb) tot[mt][tb] = mfma_bf16(xs[tb], b, tot[mt][tb]);
+        for (int tb = 0; tb < NT; ++tb) {
+            u32x4 xs[STEPS];
+            xl(tb, xs);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                one[tb] = mfma_bf16(xs[d], ones, one[tb]);
+#pragma unroll
+                for (int mt = 0; mt < NMAT; ++mt) tot[mt][tb] = mfma_bf16(xs[d], bw[mt][d], tot[mt][tb]);
             }
         }
     }
 }
 
-// Streams blocks gb = gb0 + j*step (j < nb) of a 16-row tile of NMAT matrices.
-// wq: per lane, code row base + 16*lane_group; wsp/wzp: per lane, INT4 scale
-// and zero rows as bf16 pairs (one dword per block).  xl: per lane and token
-// block, the LDS row of activations (+ 8*lane_group); block gb is at local
-// block lb = lb0 + j*step.  PF blocks of codes are kept in flight.
-template <int FMT, int NMAT, int NT, int MT, int PF>
-__device__ __forceinline__ void stream_tile(const uint8_t* const (&wq)[NMAT], const uint32_t* const (&wsp)[NMAT],
-                                            const uint32_t* const (&wzp)[NMAT], const uint16_t* const (&xl)[NT],
-                                            int nb, int gb0, int lb0, int step, f32x4 (&tot)[NMAT][NT],
-                                            f32x4 (&one)[NT])
+// Issues the staging of activation rows 0..Rc-1 of the K range (and, with
+// SZ, the INT4 scale/zero pairs of the tile) as direct global->LDS loads: one
+// wave instruction fills 64 consecutive LDS slots, lane i slot base+i.  Wave
+// w issues instructions w, w+KS, ...  Nothing waits here; the caller waits on
+// the vector memory counter and then on a barrier.  NATX: the source rows are
+// natural-order x and the chunks are gathered in consumption order (INT4
+// chunks are permuted when read); otherwise the source is already in
+// consumption order.
+template <int FMT, bool NATX, int NMAT>
+__device__ __forceinline__ void stage_issue(const Lds& L, const uint16_t* __restrict__ src, int Rc, int kb0, int nbk,
+                                            bool SZ, const MatDev (&mats)[NMAT], int e, int row0, int n, int KS,
+                                            int w)
 {
-    u32x4 rq[PF][NMAT];
-    uint32_t rs[PF][NMAT], rz[PF][NMAT];
-#pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        if (s < nb) {
-            const int gb = gb0 + s * step;
-#pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                rq[s][mt] = __builtin_nontemporal_load((const u32x4*)(wq[mt] + (size_t)gb * 64));
-                if constexpr (FMT == FMT_INT4) {
-                    rs[s][mt] = wsp[mt][gb];
-                    rz[s][mt] = wzp[mt][gb];
+    constexpr int BK = FmtT<FMT>::BK, CPB = BK / 8;
+    const int lane = threadIdx.x & 63;
+    const int per_row = L.per_row;
+    const int xslots = Rc * per_row;
+    const int nxi = uniform((xslots + 63) >> 6);
+    for (int i = w; i < nxi; i += KS) {
+        const int slot = (i << 6) + lane;
+        if (slot < xslots) {
+            const int rr = slot / per_row, jp = slot - rr * per_row;
+            const int lb = jp / CPB, ci = (jp - lb * CPB) ^ ((rr >> L.swz_shift) & L.swz_mask);
+            const uint16_t* g = src + L.roff[rr] + (kb0 + lb) * BK + (NATX ? nat_run<FMT>(ci) : ci * 8);
+            lds_dma16(g, lds_addr(L.x + (i << 10)));
+        }
+    }
+    if constexpr (FMT == FMT_INT4) {
+        if (SZ) {
+            const int K = mats[0].k;
+            const int zs = L.zstride;
+            const int zslots = 2 * NMAT * 16 * zs;
+            const int nzi = uniform((zslots + 63) >> 6);
+            for (int i = w; i < nzi; i += KS) {
+                const int slot = (i << 6) + lane;
+                const int q = slot >> 1;
+                const int mt = q / (16 * zs), rem = q - mt * 16 * zs;
+                const int r = rem / zs, lb = rem - r * zs;
+                if (slot < zslots && lb < nbk) {
+                    const bool m1 = NMAT > 1 && mt != 0;
+                    const uint16_t* zb = m1 ? mats[NMAT - 1].z : mats[0].z;
+                    const uint16_t* sb = (const uint16_t*)(m1 ? mats[NMAT - 1].s : mats[0].s);
+                    const long long se = m1 ? mats[NMAT - 1].se : mats[0].se;
+                    const uint16_t* g = ((slot & 1) ? zb : sb) + (size_t)e * se + (size_t)min(row0 + r, n - 1) * (K / 64) +
+                                        2 * (kb0 + lb);
+                    lds_dma4(g, lds_addr(L.sz + (i << 8)));
                 }
             }
         }
     }
-    for (int j0 = 0; j0 < nb; j0 += PF) {
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The K loop of this wave.  `stage` issues the staging loads (no waits);
+// the ring is primed after it, so that waiting for the staging
+// (vmcnt <= PF*NMAT) leaves the primed code loads in flight.
+template <int FMT, int NMAT, int NT, int MT, int PF, bool NATX, typename Stage>
+__device__ __forceinline__ void run_tile(const TileW<NMAT>& t, const KRange& kr, const Lds& L, int Rc, Stage stage,
+                                         f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT])
+{
+    constexpr int BK = FmtT<FMT>::BK, STEPS = FmtT<FMT>::STEPS;
+    const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+    const int nbw = pair_count(kr.nbk, kr.KS, kr.ks);
+
+    // LDS addresses of this lane's activation pieces: row base, and the
+    // swizzled position of chunk 4d+g inside a block
+    uint32_t xrow[NT];
+    uint32_t xoff_b[NT], xoff_a[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+        const int row = min(tb * 16 + lr, Rc - 1);
+        const int sw = (row >> L.swz_shift) & L.swz_mask;
+        xrow[tb] = (uint32_t)(row * L.per_row) * 16u;
+        xoff_a[tb] = (uint32_t)((sw >> 2) & (STEPS - 1));
+        xoff_b[tb] = 16u * (uint32_t)((g ^ sw) & 3);
+    }
+    const uint8_t* szrow = L.sz + (size_t)lr * L.zstride * 8;
+
+    u32x4 rq[PF][NMAT];
+    auto issue = [&](int slot, int q) {
+        q = q < nbw ? q : nbw - 1;
+        const int lb = pair_block(kr.ks, kr.KS, q);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+            rq[slot][mt] = __builtin_nontemporal_load((const u32x4*)(t.q[mt] + (size_t)lb * 64 + t.vq));
+    };
+    auto consume = [&](int slot, int q) {
+        const int lb = pair_block(kr.ks, kr.KS, q);
+        auto xl = [&](int tb, u32x4 (&xs)[STEPS]) {
+            const uint8_t* xb = L.x + xrow[tb] + (uint32_t)lb * (BK * 2) + xoff_b[tb];
+#pragma unroll
+            for (int d = 0; d < STEPS; ++d) {
+                xs[d] = *(const u32x4*)(xb + 64u * ((uint32_t)d ^ xoff_a[tb]));
+                if constexpr (NATX && FMT == FMT_INT4) xs[d] = permute_0415(xs[d]);
+            }
+        };
+        uint32_t cs[NMAT], cz[NMAT];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+            if constexpr (FMT == FMT_INT4) {
+                const u32x2 v = *(const u32x2*)(szrow + ((size_t)mt * 16 * L.zstride + lb) * 8);
+                cs[mt] = v[0];
+                cz[mt] = v[1];
+            } else {
+                cs[mt] = 0u;
+                cz[mt] = 0u;
+            }
+        }
+        compute_block<FMT, NMAT, NT, MT>(rq[slot], cs, cz, xl, tot, one);
+    };
+
+    stage();
+    __builtin_amdgcn_sched_barrier(0);
+    if (nbw > 0) {
+#pragma unroll
+        for (int s = 0; s < PF; ++s) issue(s, s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (nbw > 0)
+        wait_vmcnt<PF * NMAT>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");   // no LDS read moves above the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    int q = 0;
+    for (; q + PF <= nbw; q += PF) {
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
-            const int j = j0 + s;
-            if (j < nb) {
-                u32x4 cq[NMAT];
-                uint32_t cs[NMAT], cz[NMAT];
-#pragma unroll
-                for (int mt = 0; mt < NMAT; ++mt) {
-                    cq[mt] = rq[s][mt];
-                    cs[mt] = rs[s][mt];
-                    cz[mt] = rz[s][mt];
-                }
-                const int jn = j + PF;
-                if (jn < nb) {
-                    const int gb = gb0 + jn * step;
-#pragma unroll
-                    for (int mt = 0; mt < NMAT; ++mt) {
-                        rq[s][mt] = __builtin_nontemporal_load((const u32x4*)(wq[mt] + (size_t)gb * 64));
-                        if constexpr (FMT == FMT_INT4) {
-                            rs[s][mt] = wsp[mt][gb];
-                            rz[s][mt] = wzp[mt][gb];
-                        }
-                    }
-                }
-                compute_block<FMT, NMAT, NT, MT>(cq, cs, cz, xl, lb0 + j * step, tot, one);
-            }
+            consume(s, q + s);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(s, q + s + PF);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int s = 0; s < PF - 1; ++s)
+        if (q + s < nbw) consume(s, q + s);
+}
+
+// Lane-level code addressing for rows row0..row0+15 (clamped to n-1) from block kb0.
+template <int FMT, int NMAT>
+__device__ __forceinline__ void tile_weights(TileW<NMAT>& t, const MatDev (&mats)[NMAT], int e, int row0, int n,
+                                             int K, int kb0)
+{
+    const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+    const int wrow = min(row0 + lr, n - 1) - row0;
+    const size_t qrow = FMT == FMT_INT4 ? (size_t)K / 2 : (size_t)K;
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+        const MatDev& M = mats[mt];
+        t.q[mt] = M.q + (size_t)e * M.qe + (size_t)row0 * qrow + (size_t)kb0 * 64;
+    }
+    t.vq = (uint32_t)(wrow * qrow + 16 * g);
 }
 
 // --------------------------------------------------------------------------
@@ -226,34 +402,85 @@ struct PlanView {
     __device__ int slot_pair(int i) const { return p[2 * m + 4 + 3 * m * k + i]; }
 };
 
+struct Item {
+    int e, R, pb;
+    bool ok;
+};
+
+// Work item: union entry u (routed) or the whole batch (dense).
+__device__ __forceinline__ Item resolve_item(const PlanView& pv, bool routed, int u, int m, int act_rows,
+                                             const int32_t* topk_ids, int n_experts)
+{
+    Item it{0, m, 0, true};
+    if (!routed) return it;
+    it.pb = pv.slot_begin(u);
+    it.R = pv.slot_begin(u + 1) - it.pb;
+    if (it.R <= 0) {
+        it.ok = false;
+        return it;
+    }
+    const int p0 = pv.slot_pair(it.pb);
+    if (p0 < 0 || p0 >= act_rows) {
+        it.ok = false;
+        return it;
+    }
+    it.e = topk_ids[p0];
+    it.ok = it.e >= 0 && it.e < n_experts;
+    return it;
+}
+
+// Pair index of row li of an item (-1 if the plan entry is out of range).
+__device__ __forceinline__ int item_pair(const PlanView& pv, const Item& it, int li, int act_rows)
+{
+    const int pr = pv.slot_pair(it.pb + li);
+    return (pr >= 0 && pr < act_rows) ? pr : -1;
+}
+
+// Dynamic LDS layout shared by the kernels (the host computes the same sizes).
+struct LdsLayout {
+    int per_row, zstride;
+    size_t sz, rows, red, total;
+};
+
+__host__ __device__ inline LdsLayout lds_layout(int nmat, int fmt, int nbk, int rows_cap, int KS,
+                                                int red_floats_per_lane)
+{
+    LdsLayout l;
+    const int BK = fmt == FMT_INT4 ? 128 : 64;
+    l.per_row = nbk * BK / 8;
+    l.zstride = nbk | 1;
+    l.sz = (size_t)rows_cap * l.per_row * 16;
+    l.rows = l.sz + (fmt == FMT_INT4 ? (size_t)nmat * 16 * l.zstride * 8 : 0);
+    l.rows = (l.rows + 15) & ~(size_t)15;
+    l.red = l.rows + (size_t)rows_cap * 8;
+    l.red = (l.red + 15) & ~(size_t)15;
+    l.total = l.red + (size_t)KS * red_floats_per_lane * 64 * 4;
+    return l;
+}
+
 // --------------------------------------------------------------------------
-// gate + up + activation.  One workgroup = KS waves on one 16-row tile; the
-// waves split K (blocks w, w+KS, ...) and are reduced through LDS.  The
-// activation f(gate)*up is computed in double, rounded to fp32, split into a
-// bf16 hi/lo pair and written in the consumption order of the down matrix.
+// gate + up + activation.  One workgroup = KS waves on one 16-row tile over
+// the whole of K.  The activation f(gate)*up is computed in double, rounded
+// to fp32, split into a bf16 hi/lo pair and written in the consumption order
+// of the down matrix: act row 2r holds hi, row 2r+1 lo, of activation row r
+// (token or pair).
 
 struct GUParams {
     MatDev gate, up;
     int N, K;                  // inter, hidden
     int act;                   // 1 SiLU, 2 GELU(tanh)
-    int dfmt;                  // down matrix format: order of the act planes
+    int dfmt;                  // down matrix format: order of the act rows
     const uint16_t* x;         // [m][K] bf16
     int m;
-    int rows_cap;              // activation rows staged per pass (<= 16*NT)
-    // routed mode (plan != nullptr): items are (union entry, tile)
-    const int32_t* plan;
+    int rows_cap;              // activation rows per pass (<= 16*NT)
+    const int32_t* plan;       // routed mode: items are (union entry, tile)
     int top_k;
     const int32_t* topk_ids;
     int n_experts;
-    uint16_t* act_hi;          // [rows][N]
-    uint16_t* act_lo;
-    int act_rows;              // rows of the act planes (m, or m*top_k)
-    // dense shared-expert gate logit: logit[t] = <gate_vec, x_t>
-    const uint16_t* gate_vec;
+    uint16_t* act_out;         // [2*act_rows][N]
+    int act_rows;              // m, or m*top_k
+    const uint16_t* gate_vec;  // dense shared-expert gate: logit[t] = <gate_vec, x_t>
     float* logit;
-    // counters of the next kernel, cleared here
-    unsigned* zero_ptr;
-    int zero_count;
 };
 
 template <int FMT, int NT, int MT>
@@ -261,82 +488,60 @@ __global__ void __launch_bounds__(512) gu_kernel(GUParams p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int BK = FmtT<FMT>::BK;
-    const int KS = blockDim.x >> 6;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+    constexpr int PER = 2 * NT * 4;   // reduction floats per lane and wave
+    const int KS = uniform(blockDim.x >> 6);
+    const int w = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lr = lane & 15;
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int NB = p.K / BK;
     const int tiles = (p.N + 15) >> 4;
-    const int xstride = p.K + 8;   // elements; +16 bytes spreads LDS banks
-    uint16_t* xs = (uint16_t*)smem;
-    float* red = (float*)(smem + (size_t)p.rows_cap * xstride * 2);
-
-    for (int i = blockIdx.x * nthr + tid; i < p.zero_count; i += gridDim.x * nthr) p.zero_ptr[i] = 0u;
+    const LdsLayout LL = lds_layout(2, FMT, NB, p.rows_cap, KS, PER);
+    Lds L;
+    L.x = smem;
+    L.per_row = NB * (BK / 8);
+    set_swizzle<FMT>(L);
+    L.sz = smem + LL.sz;
+    L.zstride = NB | 1;
+    long long* roff = (long long*)(smem + LL.rows);
+    L.roff = roff;
+    float* red = (float*)(smem + LL.red);
+    const KRange kr{0, NB, KS, w};
 
     if (p.gate_vec != nullptr && blockIdx.x == 0) {
         for (int t = w; t < p.m; t += KS) {
             double acc = 0.0;
-            for (int i = lane; i < p.K; i += 64) acc += (double)bf16_f32(p.gate_vec[i]) * (double)bf16_f32(p.x[(size_t)t * p.K + i]);
+            for (int i = lane; i < p.K; i += 64)
+                acc += (double)bf16_f32(p.gate_vec[i]) * (double)bf16_f32(p.x[(size_t)t * p.K + i]);
             for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
             if (lane == 0) p.logit[t] = (float)acc;
         }
     }
 
+    const bool routed = p.plan != nullptr;
     PlanView pv{p.plan, p.m, p.top_k};
-    const int n_items = p.plan ? pv.n_union() * tiles : tiles;
+    const int n_items = routed ? pv.n_union() * tiles : tiles;
+    const MatDev mats[2] = {p.gate, p.up};
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int tile = item % tiles;
-        int R, pb = 0, e = 0;
-        if (p.plan) {
-            const int u = item / tiles;
-            pb = pv.slot_begin(u);
-            R = pv.slot_begin(u + 1) - pb;
-            if (R <= 0) continue;
-            const int p0 = pv.slot_pair(pb);
-            if (p0 < 0 || p0 >= p.m * p.top_k) continue;
-            e = p.topk_ids[p0];
-            if (e < 0 || e >= p.n_experts) continue;
-        } else {
-            R = p.m;
-        }
+        const Item it = resolve_item(pv, routed, item / tiles, p.m, p.act_rows, p.topk_ids, p.n_experts);
+        if (!it.ok) continue;
         const int row0 = tile * 16;
-        const int wrow = min(row0 + lr, p.N - 1);
-        const uint8_t* wq[2];
-        const uint32_t* wsp[2];
-        const uint32_t* wzp[2];
-        const MatDev* mats[2] = {&p.gate, &p.up};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const MatDev& M = *mats[mt];
-            if constexpr (FMT == FMT_INT4) {
-                wq[mt] = M.q + (size_t)e * M.qe + (size_t)wrow * (p.K / 2) + 16 * g;
-                wsp[mt] = (const uint32_t*)((const uint16_t*)M.s + (size_t)e * M.se + (size_t)wrow * (p.K / 64));
-                wzp[mt] = (const uint32_t*)(M.z + (size_t)e * M.se + (size_t)wrow * (p.K / 64));
-            } else {
-                wq[mt] = M.q + (size_t)e * M.qe + (size_t)wrow * p.K + 16 * g;
-                wsp[mt] = nullptr;
-                wzp[mt] = nullptr;
-            }
-        }
-        for (int c0 = 0; c0 < R; c0 += p.rows_cap) {
-            const int Rc = min(p.rows_cap, R - c0);
-            // stage activation rows c0..c0+Rc in consumption order
-            const int chunks = NB * (BK / 8);
-            for (int it = tid; it < Rc * chunks; it += nthr) {
-                const int rr = it / chunks, ci = it - rr * chunks;
-                const int lb = ci / (BK / 8), c = ci - lb * (BK / 8);
-                int src_row;
-                if (p.plan) {
-                    const int pr = pv.slot_pair(pb + c0 + rr);
-                    src_row = (pr >= 0 && pr < p.m * p.top_k) ? pr / p.top_k : 0;
-                } else {
-                    src_row = c0 + rr;
+        TileW<2> t;
+        tile_weights<FMT, 2>(t, mats, it.e, row0, p.N, p.K, 0);
+        for (int c0 = 0; c0 < it.R; c0 += p.rows_cap) {
+            const int Rc = min(p.rows_cap, it.R - c0);
+            if (tid < Rc) {
+                int tok = c0 + tid;
+                if (routed) {
+                    const int pr = item_pair(pv, it, c0 + tid, p.act_rows);
+                    tok = pr < 0 ? 0 : pr / p.top_k;
                 }
-                u32x4 v = *(const u32x4*)(p.x + (size_t)src_row * p.K + lb * BK + nat_run<FMT>(c));
-                if constexpr (FMT == FMT_INT4) v = permute_0415(v);
-                *(u32x4*)(xs + rr * xstride + lb * BK + c * 8) = v;
+                roff[tid] = (long long)tok * p.K;
             }
             __syncthreads();
-
+            auto stage = [&]() {
+                stage_issue<FMT, true, 2>(L, p.x, Rc, 0, NB, c0 == 0, mats, it.e, row0, p.N, KS, w);
+            };
             f32x4 tot[2][NT], one[NT];
 #pragma unroll
             for (int tb = 0; tb < NT; ++tb) {
@@ -344,53 +549,47 @@ __global__ void __launch_bounds__(512) gu_kernel(GUParams p)
                 tot[0][tb] = one[tb];
                 tot[1][tb] = one[tb];
             }
-            const uint16_t* xl[NT];
-#pragma unroll
-            for (int tb = 0; tb < NT; ++tb) xl[tb] = xs + min(tb * 16 + lr, Rc - 1) * xstride + 8 * g;
-            const int nb = (NB - w + KS - 1) / KS;
-            stream_tile<FMT, 2, NT, MT, 4>(wq, wsp, wzp, xl, nb, w, w, KS, tot, one);
+            run_tile<FMT, 2, NT, MT, kPfGU, true>(t, kr, L, Rc, stage, tot, one);
 
-            // cross-wave reduction
-            constexpr int PER = (FMT == FMT_INT8 ? 3 : 2) * NT * 4;   // floats per lane
+            // per-wave partials (INT8: row scale and code bias applied)
+            float sc[2] = {1.0f, 1.0f};
+            if constexpr (FMT == FMT_INT8) {
+                const int n = min(row0 + lr, p.N - 1);
+                sc[0] = ((const float*)p.gate.s)[(size_t)it.e * p.gate.se + n];
+                sc[1] = ((const float*)p.up.s)[(size_t)it.e * p.up.se + n];
+            }
 #pragma unroll
-            for (int tb = 0; tb < NT; ++tb)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    red[((w * PER) + (0 * NT + tb) * 4 + i) * 64 + lane] = tot[0][tb][i];
-                    red[((w * PER) + (1 * NT + tb) * 4 + i) * 64 + lane] = tot[1][tb][i];
-                    if constexpr (FMT == FMT_INT8) red[((w * PER) + (2 * NT + tb) * 4 + i) * 64 + lane] = one[tb][i];
-                }
+                for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = tot[mt][tb][i];
+                        if constexpr (FMT == FMT_INT8) v = sc[mt] * fmaf(-128.0f, one[tb][i], v);
+                        red[((w * PER) + (mt * NT + tb) * 4 + i) * 64 + lane] = v;
+                    }
             __syncthreads();
-            for (int it = tid; it < Rc * 16; it += nthr) {
-                const int rr = it >> 4, nl = it & 15, n = row0 + nl;
+            for (int ii = tid; ii < Rc * 16; ii += nthr) {
+                const int rr = ii >> 4, nl = ii & 15, n = row0 + nl;
                 if (n >= p.N) continue;
                 const int tb = rr >> 4, rl = rr & 15;
                 const int ln = ((rl >> 2) << 4) | nl, i = rl & 3;
-                float gs = 0.f, us = 0.f, os = 0.f;
+                float gs = 0.f, us = 0.f;
                 for (int ww = 0; ww < KS; ++ww) {
                     gs += red[((ww * PER) + (0 * NT + tb) * 4 + i) * 64 + ln];
                     us += red[((ww * PER) + (1 * NT + tb) * 4 + i) * 64 + ln];
-                    if constexpr (FMT == FMT_INT8) os += red[((ww * PER) + (2 * NT + tb) * 4 + i) * 64 + ln];
-                }
-                if constexpr (FMT == FMT_INT8) {
-                    const float sg = ((const float*)p.gate.s)[(size_t)e * p.gate.se + n];
-                    const float su = ((const float*)p.up.s)[(size_t)e * p.up.se + n];
-                    gs = sg * fmaf(-128.0f, os, gs);
-                    us = su * fmaf(-128.0f, os, us);
                 }
                 const float a = (float)(act_f64(p.act, (double)gs) * (double)us);
                 uint16_t hi, lo;
                 split_bf16(a, hi, lo);
-                int orow;
-                if (p.plan) {
-                    orow = pv.slot_pair(pb + c0 + rr);
-                    if (orow < 0 || orow >= p.act_rows) continue;
-                } else {
-                    orow = c0 + rr;
+                int orow = c0 + rr;
+                if (routed) {
+                    orow = item_pair(pv, it, c0 + rr, p.act_rows);
+                    if (orow < 0) continue;
                 }
-                const size_t o = (size_t)orow * p.N + cons_index(p.dfmt, n);
-                p.act_hi[o] = hi;
-                p.act_lo[o] = lo;
+                const size_t o = (size_t)(2 * orow) * p.N + cons_index(p.dfmt, n);
+                p.act_out[o] = hi;
+                p.act_out[o + p.N] = lo;
             }
             __syncthreads();
         }
@@ -398,40 +597,38 @@ __global__ void __launch_bounds__(512) gu_kernel(GUParams p)
 }
 
 // --------------------------------------------------------------------------
-// down + tail.  One workgroup = WR waves, each on its own 16-row tile (the
-// workgroup covers 16*WR rows), over the K range of grid row blockIdx.y.  The
-// activation rows (hi and lo planes) of that range are staged in LDS.  With
-// more than one K range the partial sums go to the workspace and the last
-// workgroup of a row group (a counter cleared by the gate/up kernel) reduces
-// them in a fixed order and applies the tail.
+// down + tail.  One workgroup = KS waves on one 16-row tile over the K range
+// of grid row blockIdx.y.  The activation rows are the interleaved hi/lo act
+// rows of the item's tokens (or pairs), so a lane holds the hi and lo sums of
+// one token in registers i and i+1.  With one K range the tail is applied
+// here; otherwise (and for the RMSNORM and routed tails) the workgroup writes
+// its fp32 partial h to part[range][row][n] for the kernel that follows.
 
 enum { TAIL_NONE = 0, TAIL_RESIDUAL = 1, TAIL_RMSNORM = 2, TAIL_SIGMOID = 3, TAIL_PAIR = 4 };
 
 struct DownParams {
     MatDev down;
     int N, K;                  // hidden, inter
-    const uint16_t* act_hi;    // [act_rows][K] consumption order
-    const uint16_t* act_lo;
+    const uint16_t* act;       // [2*act_rows][K] consumption order, hi/lo interleaved
     int act_rows;
     int m;
-    int rows_cap;              // X rows (hi + lo) staged per pass (<= 16*NT)
+    int rows_cap;              // act rows per pass (even, <= 16*NT)
+    int KG;                    // K ranges (gridDim.y)
     const int32_t* plan;       // routed mode
     int top_k;
     const int32_t* topk_ids;
     int n_experts;
-    float* partial;            // [KG][2*act_rows][N] fp32 (KG > 1)
-    unsigned* counters;        // [n_items]
     int tail;
     uint16_t* out;             // [m][N] bf16
-    float* hbuf;               // [m][N] fp32 (RMSNORM) or [act_rows][N] (PAIR)
+    float* part;               // [KG][rows][N] fp32 partial h (rows: m tokens or act_rows pairs)
     const float* logit;        // [m] (SIGMOID)
 };
 
-template <int FMT, int NT, int MT>
 __device__ __forceinline__ void down_finish(const DownParams& p, int t, int n, float h)
 {
-    if (p.tail == TAIL_PAIR || p.tail == TAIL_RMSNORM) {
-        p.hbuf[(size_t)t * p.N + n] = h;
+    if (p.KG > 1 || p.tail == TAIL_PAIR || p.tail == TAIL_RMSNORM) {
+        const size_t rows = p.tail == TAIL_PAIR ? (size_t)p.act_rows : (size_t)p.m;
+        p.part[((size_t)blockIdx.y * rows + t) * p.N + n] = h;
     } else if (p.tail == TAIL_RESIDUAL) {
         uint16_t* o = p.out + (size_t)t * p.N + n;
         *o = bf16_from_f64((double)bf16_f32(*o) + (double)h);
@@ -444,149 +641,100 @@ __device__ __forceinline__ void down_finish(const DownParams& p, int t, int n, f
 }
 
 template <int FMT, int NT, int MT>
-__global__ void __launch_bounds__(256) down_kernel(DownParams p)
+__global__ void __launch_bounds__(512) down_kernel(DownParams p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ unsigned s_last;
-    constexpr int BK = FmtT<FMT>::BK;
-    const int WR = blockDim.x >> 6;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+    constexpr int PER = NT * 2;   // token sums per lane and wave
+    const int KS = uniform(blockDim.x >> 6);
+    const int w = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lr = lane & 15;
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const int NB = p.K / BK;
-    const int KG = gridDim.y, kg = blockIdx.y;
-    const int kb0 = (int)(((long long)NB * kg) / KG), kb1 = (int)(((long long)NB * (kg + 1)) / KG);
-    const int nbl = kb1 - kb0;
-    const int xstride = nbl * BK + 8;
-    uint16_t* xs = (uint16_t*)smem;
-    float* res = (float*)(smem + (size_t)p.rows_cap * xstride * 2);   // [rows_cap][16*WR] (KG == 1)
-    const int rows_g = 16 * WR;
-    const int groups = (p.N + rows_g - 1) / rows_g;
+    const int NB = p.K / FmtT<FMT>::BK;
+    const int kb0 = (int)(((long long)NB * blockIdx.y) / p.KG), kb1 = (int)(((long long)NB * (blockIdx.y + 1)) / p.KG);
+    const int nbk = kb1 - kb0;
+    const int nbk_max = (NB + p.KG - 1) / p.KG;
+    const int tiles = (p.N + 15) >> 4;
+    const LdsLayout LL = lds_layout(1, FMT, nbk_max, p.rows_cap, KS, PER);
+    Lds L;
+    L.x = smem;
+    L.per_row = nbk * (FmtT<FMT>::BK / 8);   // this range; the layout is sized for the longest
+    set_swizzle<FMT>(L);
+    L.sz = smem + LL.sz;
+    L.zstride = nbk | 1;
+    long long* roff = (long long*)(smem + LL.rows);
+    L.roff = roff;
+    float* red = (float*)(smem + LL.red);
+    const KRange kr{kb0, nbk, KS, w};
 
+    const bool routed = p.plan != nullptr;
     PlanView pv{p.plan, p.m, p.top_k};
-    const int n_items = p.plan ? pv.n_union() * groups : groups;
+    const int n_items = routed ? pv.n_union() * tiles : tiles;
+    const MatDev mats[1] = {p.down};
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int grp = item % groups;
-        int R, pb = 0, e = 0;
-        if (p.plan) {
-            const int u = item / groups;
-            pb = pv.slot_begin(u);
-            R = pv.slot_begin(u + 1) - pb;
-            if (R <= 0) continue;
-            const int p0 = pv.slot_pair(pb);
-            if (p0 < 0 || p0 >= p.act_rows) continue;
-            e = p.topk_ids[p0];
-            if (e < 0 || e >= p.n_experts) continue;
-        } else {
-            R = p.m;
-        }
-        const int R2 = 2 * R;                  // hi rows then lo rows
-        const int row0 = grp * rows_g + w * 16;
-        const int wrow = min(row0 + lr, p.N - 1);
-        const MatDev& M = p.down;
-        const uint8_t* wq[1];
-        const uint32_t* wsp[1];
-        const uint32_t* wzp[1];
-        if constexpr (FMT == FMT_INT4) {
-            wq[0] = M.q + (size_t)e * M.qe + (size_t)wrow * (p.K / 2) + 16 * g;
-            wsp[0] = (const uint32_t*)((const uint16_t*)M.s + (size_t)e * M.se + (size_t)wrow * (p.K / 64));
-            wzp[0] = (const uint32_t*)(M.z + (size_t)e * M.se + (size_t)wrow * (p.K / 64));
-        } else {
-            wq[0] = M.q + (size_t)e * M.qe + (size_t)wrow * p.K + 16 * g;
-            wsp[0] = nullptr;
-            wzp[0] = nullptr;
-        }
+        const int tile = item % tiles;
+        const Item it = resolve_item(pv, routed, item / tiles, p.m, p.act_rows, p.topk_ids, p.n_experts);
+        if (!it.ok) continue;
+        const int row0 = tile * 16;
+        TileW<1> t;
+        tile_weights<FMT, 1>(t, mats, it.e, row0, p.N, p.K, kb0);
+        float sc = 1.0f;
+        if constexpr (FMT == FMT_INT8) sc = ((const float*)p.down.s)[(size_t)it.e * p.down.se + min(row0 + lr, p.N - 1)];
+        const int R2 = 2 * it.R;
         for (int c0 = 0; c0 < R2; c0 += p.rows_cap) {
-            const int Rc = min(p.rows_cap, R2 - c0);
-            const int chunks = nbl * (BK / 8);
-            for (int it = tid; it < Rc * chunks; it += nthr) {
-                const int rr = it / chunks, ci = it - rr * chunks;
-                const int xr = c0 + rr;
-                const int li = xr < R ? xr : xr - R;
-                int arow;
-                if (p.plan) {
-                    arow = pv.slot_pair(pb + li);
-                    if (arow < 0 || arow >= p.act_rows) arow = 0;
-                } else {
-                    arow = li;
+            const int Rc = min(p.rows_cap, R2 - c0);   // even
+            if (tid < Rc) {
+                const int xr = c0 + tid, li = xr >> 1;
+                int arow = li;
+                if (routed) {
+                    arow = item_pair(pv, it, li, p.act_rows);
+                    if (arow < 0) arow = 0;
                 }
-                const uint16_t* src = (xr < R ? p.act_hi : p.act_lo) + (size_t)arow * p.K + kb0 * BK + ci * 8;
-                *(u32x4*)(xs + rr * xstride + ci * 8) = *(const u32x4*)src;
+                roff[tid] = (long long)(2 * arow + (xr & 1)) * p.K;
             }
             __syncthreads();
-
+            auto stage = [&]() {
+                stage_issue<FMT, false, 1>(L, p.act, Rc, kb0, nbk, c0 == 0, mats, it.e, row0, p.N, KS, w);
+            };
             f32x4 tot[1][NT], one[NT];
 #pragma unroll
             for (int tb = 0; tb < NT; ++tb) {
                 one[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 tot[0][tb] = one[tb];
             }
-            const uint16_t* xl[NT];
-#pragma unroll
-            for (int tb = 0; tb < NT; ++tb) xl[tb] = xs + min(tb * 16 + lr, Rc - 1) * xstride + 8 * g;
-            if (row0 < p.N) stream_tile<FMT, 1, NT, MT, 6>(wq, wsp, wzp, xl, nbl, kb0, 0, 1, tot, one);
+            run_tile<FMT, 1, NT, MT, (NT >= 4 ? 4 : kPfDN), false>(t, kr, L, Rc, stage, tot, one);
 
-            // per-lane results: weight row row0 + lr, X rows c0 + tb*16 + 4g + i
-            float sc = 1.0f;
-            if constexpr (FMT == FMT_INT8) sc = ((const float*)M.s)[(size_t)e * M.se + wrow];
+            // lane: weight row row0+lr, act rows tb*16 + 4g + i; hi (i even) + lo (i odd)
 #pragma unroll
             for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = tb * 16 + 4 * g + i;
-                    if (rr >= Rc || row0 + lr >= p.N) continue;
-                    float v = tot[0][tb][i];
-                    if constexpr (FMT == FMT_INT8) v = sc * fmaf(-128.0f, one[tb][i], v);
-                    const int xr = c0 + rr;
-                    if (KG == 1) {
-                        res[xr * rows_g + w * 16 + lr] = v;
-                    } else {
-                        int prow;   // partial row: hi rows [0, act_rows), lo rows [act_rows, 2*act_rows)
-                        const int li = xr < R ? xr : xr - R;
-                        if (p.plan) prow = pv.slot_pair(pb + li);
-                        else prow = li;
-                        if (prow < 0 || prow >= p.act_rows) continue;
-                        if (xr >= R) prow += p.act_rows;
-                        p.partial[((size_t)kg * 2 * p.act_rows + prow) * p.N + row0 + lr] = v;
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    float vh = tot[0][tb][2 * h2], vl = tot[0][tb][2 * h2 + 1];
+                    if constexpr (FMT == FMT_INT8) {
+                        vh = sc * fmaf(-128.0f, one[tb][2 * h2], vh);
+                        vl = sc * fmaf(-128.0f, one[tb][2 * h2 + 1], vl);
                     }
+                    red[((w * PER) + tb * 2 + h2) * 64 + lane] = vh + vl;
                 }
             __syncthreads();
-        }
-        // finish: sum the hi and lo rows (and the K ranges) and apply the tail
-        bool finisher = (KG == 1);
-        if (KG > 1) {
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) s_last = atomicAdd(&p.counters[item], 1u);
-            __syncthreads();
-            finisher = (s_last == (unsigned)(KG - 1));
-            if (finisher) __threadfence();
-        }
-        if (finisher) {
-            for (int it = tid; it < R * rows_g; it += nthr) {
-                const int li = it / rows_g, nl = it - li * rows_g, n = grp * rows_g + nl;
+            const int Tc = Rc >> 1;   // tokens in this pass
+            for (int ii = tid; ii < Tc * 16; ii += nthr) {
+                const int tr = ii >> 4, nl = ii & 15, n = row0 + nl;
                 if (n >= p.N) continue;
-                int trow;
-                if (p.plan) {
-                    trow = pv.slot_pair(pb + li);
-                    if (trow < 0 || trow >= p.act_rows) continue;
-                } else {
-                    trow = li;
+                const int xr = 2 * tr;                 // hi row within the pass
+                const int tb = xr >> 4, rl = xr & 15;
+                const int ln = ((rl >> 2) << 4) | nl, h2 = (rl & 3) >> 1;
+                float h = 0.f;
+                for (int ww = 0; ww < KS; ++ww) h += red[((ww * PER) + tb * 2 + h2) * 64 + ln];
+                const int li = (c0 >> 1) + tr;
+                int trow = li;
+                if (routed) {
+                    trow = item_pair(pv, it, li, p.act_rows);
+                    if (trow < 0) continue;
                 }
-                float h;
-                if (KG == 1) {
-                    h = res[li * rows_g + nl] + res[(R + li) * rows_g + nl];
-                } else {
-                    h = 0.f;
-                    for (int q = 0; q < KG; ++q) {
-                        const float* P = p.partial + (size_t)q * 2 * p.act_rows * p.N;
-                        h += __builtin_nontemporal_load(P + (size_t)trow * p.N + n) +
-                             __builtin_nontemporal_load(P + (size_t)(p.act_rows + trow) * p.N + n);
-                    }
-                }
-                down_finish<FMT, NT, MT>(p, trow, n, h);
+                down_finish(p, trow, n, h);
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 

@@ -1,30 +1,65 @@
-// tail.h -- row-wise tails of libffnq that need a whole output row.
+// tail.h -- row-wise tails of libffnq that run after the down projection.
+// The down kernel leaves fp32 partial sums part[r][row][i] over R K-ranges;
+// these kernels add them in a fixed order (r = 0, 1, ...) before the tail.
 #pragma once
 #include "device.h"
 
 namespace ffnq {
 
-// RMSNorm with a bf16 weight over rows of h (fp32):
+__device__ __forceinline__ float sum_parts(const float* part, int R, size_t stride, size_t idx)
+{
+    float h = part[idx];
+    for (int r = 1; r < R; ++r) h += part[(size_t)r * stride + idx];
+    return h;
+}
+
+// RMSNorm with a bf16 weight over rows of h:
 //   out[t][i] = bf16(h[t][i] / sqrt(mean_i h^2 + eps) * w[i])
 // ([gemma4/shared_expert.rs] encode_rms_norm_bf16w with RMS_EPS).  The sum
 // of squares, the scale and the product are formed in double; the result is
 // rounded to bf16 once.  One workgroup per row.
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ h, const uint16_t* __restrict__ w,
-                                                      uint16_t* __restrict__ out, int n, float eps)
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ part, int R, int m,
+                                                      const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
+                                                      int n, float eps)
 {
-    __shared__ double part[256 / 64];
+    __shared__ double partial[256 / 64];
     const int t = blockIdx.x, tid = threadIdx.x;
-    const float* row = h + (size_t)t * n;
+    const size_t stride = (size_t)m * n;
     double ss = 0.0;
-    for (int i = tid; i < n; i += blockDim.x) ss += (double)row[i] * (double)row[i];
+    for (int i = tid; i < n; i += blockDim.x) {
+        const double h = sum_parts(part, R, stride, (size_t)t * n + i);
+        ss += h * h;
+    }
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    if ((tid & 63) == 0) partial[tid >> 6] = ss;
     __syncthreads();
     double tot = 0.0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += partial[i];
     const double r = 1.0 / sqrt(tot / (double)n + (double)eps);
-    for (int i = tid; i < n; i += blockDim.x)
-        out[(size_t)t * n + i] = bf16_from_f64((double)row[i] * r * (double)bf16_f32(w[i]));
+    for (int i = tid; i < n; i += blockDim.x) {
+        const double h = sum_parts(part, R, stride, (size_t)t * n + i);
+        out[(size_t)t * n + i] = bf16_from_f64(h * r * (double)bf16_f32(w[i]));
+    }
+}
+
+// Dense tails after a K-split down projection: raw residual add
+// ([llama/dense.rs] encode_residual_add), the sigmoid scalar gate
+// ([qwen/moe_batch.rs] encode_sigmoid_scalar_mul) or a plain bf16 store.
+__global__ void __launch_bounds__(256) ksum_tail_kernel(const float* __restrict__ part, int R, int m, int n, int tail,
+                                                        uint16_t* __restrict__ out, const float* __restrict__ logit)
+{
+    const size_t total = (size_t)m * n;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+        const double h = (double)sum_parts(part, R, total, idx);
+        if (tail == 1) {
+            out[idx] = bf16_from_f64((double)bf16_f32(out[idx]) + h);
+        } else if (tail == 3) {
+            const double sg = 1.0 / (1.0 + exp(-(double)logit[idx / n]));
+            out[idx] = bf16_from_f64(h * sg);
+        } else {
+            out[idx] = bf16_from_f64(h);
+        }
+    }
 }
 
 // The seeded phase-2 reduction and the raw residual add of the routed half
@@ -33,13 +68,14 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 // tail is one residual add, no norm).  d = down_e(act_p) per pair p comes from
 // the grouped down kernel.  Product and sum are each rounded to fp32
 // (no fused multiply-add), in rank order.
-__global__ void __launch_bounds__(256) moe_reduce_kernel(const float* __restrict__ pair_out,
+__global__ void __launch_bounds__(256) moe_reduce_kernel(const float* __restrict__ part, int R,
                                                          const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ topk_ids, int n_experts,
                                                          const uint16_t* __restrict__ seed, uint16_t* __restrict__ resid,
                                                          int m, int k, int n)
 {
     const size_t total = (size_t)m * n;
+    const size_t stride = (size_t)m * k * n;
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
         const int t = (int)(idx / n), i = (int)(idx - (size_t)t * n);
         float acc = seed ? bf16_f32(seed[idx]) : 0.0f;
@@ -47,8 +83,8 @@ __global__ void __launch_bounds__(256) moe_reduce_kernel(const float* __restrict
             const int p = t * k + r;
             const int e = topk_ids[p];
             if (e < 0 || e >= n_experts) continue;
-            const float prod = __fmul_rn(topk_w[p], pair_out[(size_t)p * n + i]);
-            acc = __fadd_rn(acc, prod);
+            const float d = sum_parts(part, R, stride, (size_t)p * n + i);
+            acc = __fadd_rn(acc, __fmul_rn(topk_w[p], d));
         }
         resid[idx] = bf16_from_f64((double)bf16_f32(resid[idx]) + (double)acc);
     }
