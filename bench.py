@@ -8,11 +8,22 @@ resident in HBM.  Steps rotate over several distinct copies of the layer's
 weights (more bytes than the 256 MB Infinity Cache) so each step streams its
 weights from HBM, as consecutive layers of a model do.
 
+The roofline object is for the dominant kernel (the gate/up kernel): its
+algorithmic bytes (gate and up codes, scales and zeros, plus x) divided by its
+average duration, timed live with HIP events that the library records around
+its kernels on the call's stream (ffnq_set_phase_events: the events are
+attached to the kernel dispatches, so they time the kernel itself).  `traffic` is the
+HBM byte count of that kernel from rocprofv3 FETCH_SIZE + WRITE_SIZE counters,
+scaled by the same counters on a plain copy of known size; it is read from
+profiles/ and reported only while the kernel sources are the ones it was
+measured on, else null.
+
 Prints one JSON line.  --gpus above 1 is refused: this benchmark runs on one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("moe_expert_dequant_amd/csrc/qgemm.h", "moe_expert_dequant_amd/csrc/device.h",
+                  "moe_expert_dequant_amd/csrc/ffnq.hip")
+TRAFFIC_FILE = "profiles/traffic_gu_kernel_int4_llama3-8b_m1.txt"
 
 
 def weight_bytes(fmt: int, n: int, k: int) -> int:
@@ -39,13 +53,45 @@ def layer_bytes(hidden: int, inter: int, fmt: int, m: int) -> int:
     return w + m * hidden * 2 + 2 * m * hidden * 2
 
 
-def run_gpu(m: int, steps: int, warmup: int, copies: int, seed: int = 1):
+def gu_bytes(hidden: int, inter: int, fmt: int, m: int) -> int:
+    """Algorithmic bytes of the gate/up kernel: gate and up weights once, x read.
+    (The fp32 activation it hands to the down kernel is an intermediate.)"""
+    return 2 * weight_bytes(fmt, inter, hidden) + m * hidden * 2
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """Measured HBM bytes per gate/up launch at M=1, if still valid for these sources."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256") != sources_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def setup(m: int, copies: int):
     import torch
     import gen
     import moe_expert_dequant_amd as fq
 
     c = gen.CONFIGS[1]
-    hidden, inter, fmt = c["hidden"], c["inter"], c["fmt"]
     inp = gen.config_inputs(1, m)
     base = {n: fq.to_device(inp["ffn"][n]) for n in ("gate", "up", "down")}
     layers = []
@@ -59,11 +105,20 @@ def run_gpu(m: int, steps: int, warmup: int, copies: int, seed: int = 1):
     stream = torch.cuda.current_stream()
 
     def step(i):
-        fq.dense(layers[i % copies][1], hidden, inter, m, c["act"], c["tail"], x, resid, ws=ws, stream=stream)
+        fq.dense(layers[i % copies][1], c["hidden"], c["inter"], m, c["act"], c["tail"], x, resid, ws=ws,
+                 stream=stream)
 
+    return c, step, stream
+
+
+def run_gpu(m: int, steps: int, warmup: int, copies: int):
+    """Headline pass: wall clock over `steps` back-to-back calls, plus HIP
+    events around each call."""
+    import torch
+
+    c, step, stream = setup(m, copies)
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -75,7 +130,36 @@ def run_gpu(m: int, steps: int, warmup: int, copies: int, seed: int = 1):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, per_call_ms, layer_bytes(hidden, inter, fmt, m)
+    return wall, per_call_ms, layer_bytes(c["hidden"], c["inter"], c["fmt"], m)
+
+
+def run_phases(m: int, steps: int, warmup: int, copies: int):
+    """Per-kernel pass: the library records events before/after its kernels."""
+    import torch
+    import moe_expert_dequant_amd as fq
+
+    c, step, stream = setup(m, copies)
+    for i in range(warmup):
+        step(i)
+    evs = [fq.PhaseEvents(stream) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        with evs[i]:
+            step(i)
+    torch.cuda.synchronize()
+    d = np.array([e.durations() for e in evs])   # ms: gate/up kernel, down kernel
+    return d.mean(axis=0), gu_bytes(c["hidden"], c["inter"], c["fmt"], m)
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -95,7 +179,7 @@ def cpu_baseline(budget_s: float = 12.0):
         if el >= budget_s or n >= 64:
             break
     return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{n} single-token calls (M=1) of the llama3-8b-shaped INT4 FFN layer, {el:.1f} s")
+                sample=f"{n} single-token calls (M=1) of the llama3-8b-shaped INT4 FFN layer, {el:.1f} s, one thread")
 
 
 def main():
@@ -106,7 +190,8 @@ def main():
     ap.add_argument("--m", type=int, default=1, help="tokens per call for the headline value")
     ap.add_argument("--copies", type=int, default=8, help="distinct weight copies rotated over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--single", action="store_true", help="time only --m (for profiling runs)")
+    ap.add_argument("--single", action="store_true", help="time only --m, headline pass only (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is a "
@@ -117,6 +202,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     res = {}
     for m in ([args.m] if args.single else sorted({args.m, 1, 4})):
@@ -124,10 +212,14 @@ def main():
         avg = float(np.mean(per_call)) * 1e-3
         res[m] = dict(wall=wall, avg_s=avg, med_s=float(np.median(per_call)) * 1e-3, bytes=nbytes,
                       p10_s=float(np.percentile(per_call, 10)) * 1e-3, p90_s=float(np.percentile(per_call, 90)) * 1e-3)
+    phases = {}
+    if not args.single:
+        for m in res:
+            ms, gb = run_phases(m, min(args.steps, 100), args.warmup, args.copies)
+            phases[m] = dict(gu_us=ms[0] * 1e3, down_us=ms[1] * 1e3, gu_bytes=gb)
 
     h = res[args.m]
     value = args.m * args.steps / h["wall"]
-    achieved = h["bytes"] / h["avg_s"] / 1e9
     out = {
         "metric": "quantized FFN layer tokens/s + achieved HBM GB/s (% of peak) at M=1 and M=4",
         "value": value,
@@ -148,22 +240,29 @@ def main():
             "weight_copies_rotated": args.copies,
             "parallelism": "single GPU",
         },
-        "roofline": {
+    }
+    if args.m in phases:
+        p = phases[args.m]
+        achieved = p["gu_bytes"] / (p["gu_us"] * 1e-6) / 1e9
+        traffic = read_traffic() if args.m == 1 else None
+        out["roofline"] = {
             "bound": "hbm",
-            "kernel": "ffnq_dense call (gu_kernel + down_kernel, HIP events around each call)",
+            "kernel": "gu_kernel<INT4,1,1> (gate+up dequant GEMV + SiLU gate-multiply)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-        },
-        "per_m": {str(m): {"tokens_per_s": m / r["avg_s"], "call_us_mean": r["avg_s"] * 1e6,
-                           "call_us_median": r["med_s"] * 1e6, "call_us_p10": r["p10_s"] * 1e6,
-                           "call_us_p90": r["p90_s"] * 1e6, "bytes_per_call": r["bytes"],
-                           "achieved_GBs": r["bytes"] / r["avg_s"] / 1e9,
-                           "frac_of_peak": r["bytes"] / r["avg_s"] / 1e9 / HBM_PEAK_GBS}
-                  for m, r in res.items()},
-    }
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": p["gu_bytes"],
+            "avg_launch_us": p["gu_us"],
+        }
+    out["per_m"] = {str(m): {"tokens_per_s": m / r["avg_s"], "call_us_mean": r["avg_s"] * 1e6,
+                             "call_us_median": r["med_s"] * 1e6, "call_us_p10": r["p10_s"] * 1e6,
+                             "call_us_p90": r["p90_s"] * 1e6, "bytes_per_call": r["bytes"],
+                             "achieved_GBs": r["bytes"] / r["avg_s"] / 1e9,
+                             "frac_of_peak": r["bytes"] / r["avg_s"] / 1e9 / HBM_PEAK_GBS,
+                             **({k: v for k, v in phases[m].items()} if m in phases else {})}
+                    for m, r in res.items()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

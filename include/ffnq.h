@@ -20,7 +20,9 @@
  *   - Every device pointer must be 16-byte aligned (128-bit loads).  Tensors are
  *     contiguous and row-major, with no strides.
  *   - Ownership: the caller allocates every buffer.  The library allocates,
- *     frees and synchronises nothing and keeps no state between calls.  Calls
+ *     frees and synchronises nothing and keeps no state between calls (the
+ *     one exception, ffnq_set_phase_events, is a per-thread timing switch
+ *     that never changes a result).  Calls
  *     are asynchronous on `stream`; the caller keeps every buffer alive (and
  *     unmodified, for inputs) until the stream's work has completed -- the ABI
  *     form of the pages' rule that weight memory must outlive in-flight work
@@ -230,6 +232,18 @@ FFNQ_API int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int
 
 /* Human-readable name of a status code (static string). */
 FFNQ_API const char* ffnq_status_string(int status);
+
+/* ---- per-kernel timing (profiling harnesses) ------------------------------
+ * While `ev` is non-NULL on the calling thread, every ffnq_dense,
+ * ffnq_shared_expert and ffnq_moe_routed_batched call made from that thread
+ * launches its gate/up kernel with start/stop events ev[0]/ev[1] and its down
+ * kernel with ev[2]/ev[3] (hipExtLaunchKernel: the timestamps are taken by
+ * the kernel dispatch itself, so the elapsed time is the kernel's own
+ * duration).  The four events belong to the caller (hipEventCreate, or a
+ * framework's events, valid on the stream's device); the array must stay
+ * valid until it is cleared.  NULL clears.  Returns FFNQ_OK.  Results never
+ * depend on this switch. */
+FFNQ_API int ffnq_set_phase_events(hipEvent_t* ev);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ TAIL_SIGMOID_GATE = 3
 
 OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
-EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_status_string")
+EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_status_string",
+           "ffnq_set_phase_events")
 
 
 def plan_ints(m: int, k: int) -> int:
@@ -69,6 +70,8 @@ def lib():
             getattr(L, f).restype = C.c_int
         L.ffnq_status_string.argtypes = [C.c_int]
         L.ffnq_status_string.restype = C.c_char_p
+        L.ffnq_set_phase_events.argtypes = [vp]
+        L.ffnq_set_phase_events.restype = C.c_int
         _lib = L
     return _lib
 
@@ -102,6 +105,34 @@ def ffn_struct(mats: dict) -> Ffn:
 def _check(fn: str, rc: int):
     if rc != OK:
         raise FfnqError(fn, rc)
+
+
+class PhaseEvents:
+    """Four torch timing events that the library attaches to its kernel
+    launches (ffnq_set_phase_events): start/stop of the gate/up kernel and
+    start/stop of the down kernel.
+
+    Use as a context manager around one call; afterwards (once the stream is
+    synchronised) durations() gives (gate/up, down) kernel times in ms."""
+
+    def __init__(self, stream=None):
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in self.ev:   # torch creates the underlying hipEvent_t on first record
+            e.record(self.stream)
+        self.arr = (C.c_void_p * 4)(*[e.cuda_event for e in self.ev])
+
+    def __enter__(self):
+        _check("ffnq_set_phase_events", lib().ffnq_set_phase_events(C.cast(self.arr, C.c_void_p)))
+        return self
+
+    def __exit__(self, *exc):
+        lib().ffnq_set_phase_events(None)
+        return False
+
+    def durations(self):
+        e = self.ev
+        return e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3])
 
 
 class Workspace:

@@ -2,6 +2,7 @@
 // configuration and kernel launches.  Every check runs on the host before the
 // first launch; the library allocates nothing and synchronises nothing.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <atomic>
@@ -22,6 +23,13 @@ using namespace ffnq;
 constexpr size_t kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Per-thread timing switch (ffnq_set_phase_events): start/stop events of the
+// gate/up kernel (ev[0], ev[1]) and of the down kernel (ev[2], ev[3]),
+// recorded by the kernel dispatch itself (hipExtLaunchKernel).
+thread_local hipEvent_t* t_phase_ev = nullptr;
+
+hipEvent_t phase_event(int i) { return t_phase_ev ? t_phase_ev[i] : nullptr; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -180,7 +188,8 @@ KConfig down_config(int fmt, int K, int N, long long items_est, int rows_total, 
 
 #define FFNQ_GU_CASE(F, NT_, MT_)                                                              \
     if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                              \
-        hipLaunchKernelGGL((gu_kernel<F, NT_, MT_>), grid, block, c.lds, stream, prm);         \
+        hipExtLaunchKernelGGL((gu_kernel<F, NT_, MT_>), grid, block, c.lds, stream, phase_event(0), \
+                              phase_event(1), 0, prm);                                          \
         return true;                                                                           \
     }
 
@@ -196,7 +205,8 @@ bool launch_gu(int fmt, const KConfig& c, long long items, int N, hipStream_t st
 
 #define FFNQ_DOWN_CASE(F, NT_, MT_)                                                            \
     if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                              \
-        hipLaunchKernelGGL((down_kernel<F, NT_, MT_>), grid, block, c.lds, stream, prm);       \
+        hipExtLaunchKernelGGL((down_kernel<F, NT_, MT_>), grid, block, c.lds, stream, phase_event(2), \
+                              phase_event(3), 0, prm);                                            \
         return true;                                                                           \
     }
 
@@ -364,6 +374,12 @@ const char* ffnq_status_string(int status)
     }
 }
 
+int ffnq_set_phase_events(hipEvent_t* ev)
+{
+    t_phase_ev = ev;
+    return FFNQ_OK;
+}
+
 int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail, const uint16_t* x, uint16_t* out,
                const uint16_t* norm_w, float eps, void* ws, size_t* ws_bytes, hipStream_t stream)
 {
@@ -476,7 +492,8 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     const int rgrid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
     hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, dc.kg, topk_w, topk_ids,
                        n_experts, seed, resid, m, top_k, hidden);
-    return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    return FFNQ_OK;
 }
 
 }  // extern "C"
