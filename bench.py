@@ -8,6 +8,8 @@ resident in HBM.  Steps rotate over several distinct copies of the layer's
 weights (more bytes than the 256 MB Infinity Cache) so each step streams its
 weights from HBM, as consecutive layers of a model do.
 
+The weights are packed once per copy into the tiled layout (ffnq_pack, at
+set-up, untimed: model-load work); --rowmajor streams the row-major layout.
 The roofline object is for the dominant kernel (the gate/up kernel): its
 algorithmic bytes (gate and up codes, scales and zeros, plus x) divided by its
 average duration, timed live with HIP events that the library records around
@@ -86,7 +88,7 @@ def read_traffic():
         return None
 
 
-def setup(m: int, copies: int):
+def setup(m: int, copies: int, tiled: bool = True):
     import torch
     import gen
     import moe_expert_dequant_amd as fq
@@ -95,10 +97,12 @@ def setup(m: int, copies: int):
     inp = gen.config_inputs(1, m)
     base = {n: fq.to_device(inp["ffn"][n]) for n in ("gate", "up", "down")}
     layers = []
-    for i in range(copies):
-        d = {n: {kk: (v.clone() if isinstance(v, torch.Tensor) else v) for kk, v in base[n].items()}
-             for n in base} if i else base
+    for i in range(copies):   # each copy is packed into its own tiled buffer (model-load time, not timed)
+        d = {n: fq.pack(base[n]) for n in base} if tiled else \
+            {n: {kk: (v.clone() if isinstance(v, torch.Tensor) else v) for kk, v in base[n].items()} for n in base}
         layers.append((d, fq.ffn_struct(d)))
+    del base
+    torch.cuda.synchronize()
     x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
     resid = torch.from_numpy(inp["resid"].view(np.int16)).cuda()
     ws = fq.Workspace()
@@ -111,12 +115,12 @@ def setup(m: int, copies: int):
     return c, step, stream
 
 
-def run_gpu(m: int, steps: int, warmup: int, copies: int):
+def run_gpu(m: int, steps: int, warmup: int, copies: int, tiled: bool = True):
     """Headline pass: wall clock over `steps` back-to-back calls, plus HIP
     events around each call."""
     import torch
 
-    c, step, stream = setup(m, copies)
+    c, step, stream = setup(m, copies, tiled)
     for i in range(warmup):
         step(i)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -133,12 +137,12 @@ def run_gpu(m: int, steps: int, warmup: int, copies: int):
     return wall, per_call_ms, layer_bytes(c["hidden"], c["inter"], c["fmt"], m)
 
 
-def run_phases(m: int, steps: int, warmup: int, copies: int):
+def run_phases(m: int, steps: int, warmup: int, copies: int, tiled: bool = True):
     """Per-kernel pass: the library records events before/after its kernels."""
     import torch
     import moe_expert_dequant_amd as fq
 
-    c, step, stream = setup(m, copies)
+    c, step, stream = setup(m, copies, tiled)
     for i in range(warmup):
         step(i)
     evs = [fq.PhaseEvents(stream) for _ in range(steps)]
@@ -192,6 +196,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single", action="store_true", help="time only --m, headline pass only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--rowmajor", action="store_true", help="stream the row-major weights instead of the tiled ones")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is a "
@@ -208,14 +213,14 @@ def main():
 
     res = {}
     for m in ([args.m] if args.single else sorted({args.m, 1, 4})):
-        wall, per_call, nbytes = run_gpu(m, args.steps, args.warmup, args.copies)
+        wall, per_call, nbytes = run_gpu(m, args.steps, args.warmup, args.copies, not args.rowmajor)
         avg = float(np.mean(per_call)) * 1e-3
         res[m] = dict(wall=wall, avg_s=avg, med_s=float(np.median(per_call)) * 1e-3, bytes=nbytes,
                       p10_s=float(np.percentile(per_call, 10)) * 1e-3, p90_s=float(np.percentile(per_call, 90)) * 1e-3)
     phases = {}
     if not args.single:
         for m in res:
-            ms, gb = run_phases(m, min(args.steps, 100), args.warmup, args.copies)
+            ms, gb = run_phases(m, min(args.steps, 100), args.warmup, args.copies, not args.rowmajor)
             phases[m] = dict(gu_us=ms[0] * 1e3, down_us=ms[1] * 1e3, gu_bytes=gb)
 
     h = res[args.m]
@@ -238,6 +243,7 @@ def main():
                         f"residual tail, M={args.m}",
             "m": args.m,
             "weight_copies_rotated": args.copies,
+            "weight_layout": "row-major" if args.rowmajor else "tiled (ffnq_pack, once per copy, untimed)",
             "parallelism": "single GPU",
         },
     }
@@ -247,7 +253,8 @@ def main():
         traffic = read_traffic() if args.m == 1 else None
         out["roofline"] = {
             "bound": "hbm",
-            "kernel": "gu_kernel<INT4,1,1> (gate+up dequant GEMV + SiLU gate-multiply)",
+            "kernel": ("gu_kernel" if args.rowmajor else "gu_tiled_kernel") +
+                      "<INT4,1,1> (gate+up dequant GEMV + SiLU gate-multiply)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -81,6 +81,34 @@ extern "C" {
 #define FFNQ_FMT_INT8_ROW         1
 #define FFNQ_FMT_INT4_AFFINE_G64  2
 
+/* ---- tiled formats (the layout the GPU streams fastest) ---------------------
+ * The same numbers as the two formats above, rearranged once by ffnq_pack so
+ * that every load of the K loop reads 1 KB of contiguous memory and every
+ * lane receives the codes its matrix-core step multiplies, in input order.
+ * Each 16-row tile (rows >= n of the last tile are zero) is a run of 1 KB
+ * steps; in a code step, the 16 bytes at [16*(16g + r), +16) belong to row r
+ * (r = 0..15) and lane group g (g = 0..3), as four 32-bit words w[0..3]:
+ *   FFNQ_FMT_INT8_ROW_TILED (k % 64 == 0): step b = code block b (inputs
+ *     64b..64b+63); w[2d + h] holds the int8 codes of inputs
+ *     64b + 32d + 8g + 4h + i (i = 0..3) in byte i (d, h = 0..1).  After all
+ *     tiles: the fp32 row scales, padded to 16 per tile, then to a multiple
+ *     of 256 bytes.
+ *   FFNQ_FMT_INT4_AFFINE_G64_TILED (k % 128 == 0): code blocks of 128 inputs
+ *     in groups of 8; group j is preceded by its scale/zero step (step 9j):
+ *     block bi of the group, row r at bytes [128*bi + 8*r, +8) =
+ *     {s[r][2b], s[r][2b+1]} then {z[r][2b], z[r][2b+1]} as bf16 pairs
+ *     (b = 8j + bi; unused slots of a short last group are zero).  Code block
+ *     b is step 9j + 1 + bi: w[d] holds the codes of inputs 128b + 32d + 8g + e
+ *     (e = 0..7), code e = 2v in bits [4v, 4v+4) and e = 2v+1 in bits
+ *     [16+4v, 20+4v) (v = 0..3).
+ * A tiled ffnq_qmat has q = the packed buffer and s = z = NULL; stacked
+ * experts follow each other ffnq_packed_bytes(fmt, n, k) bytes apart.  The
+ * per-byte weight traffic is that of the row-major format (plus the zero
+ * padding of a short last group or tile).
+ */
+#define FFNQ_FMT_INT8_ROW_TILED         3
+#define FFNQ_FMT_INT4_AFFINE_G64_TILED  4
+
 /* ---- gated activation, act = f(gate) * up  --------------------------------
  * The gate projection is the operand passed through f ([llama/dense.rs]: the
  * `encode_silu_mul` / `encode_gelu_mul` call takes ffn_gate first).
@@ -105,7 +133,8 @@ extern "C" {
 /* One quantized matrix of n output rows and k inputs.  For stacked expert
  * tensors the pointers address expert 0 and expert e starts at
  *   q + e*n*k (INT8) or q + e*n*k/2 (INT4) bytes,
- *   s + e*n   (INT8, fp32) or s + e*n*(k/64) (INT4, bf16) elements, z likewise. */
+ *   s + e*n   (INT8, fp32) or s + e*n*(k/64) (INT4, bf16) elements, z likewise;
+ * for a tiled format at q + e*ffnq_packed_bytes(fmt, n, k) (s, z unused). */
 typedef struct ffnq_qmat {
     int32_t fmt;      /* FFNQ_FMT_* */
     int32_t n;        /* output rows */
@@ -118,7 +147,8 @@ typedef struct ffnq_qmat {
 /* A gated FFN: gate and up are [inter][hidden], down is [hidden][inter]
  * ([gemma4/shared_expert.rs]: gate/up GEMVs take rows=inter, cols=hidden; the
  * down GEMV takes rows=hidden, cols=inter).  gate and up must share a format;
- * down may use another (per-tensor block type, [llama/dense.rs] module doc). */
+ * down may use another (per-tensor block type, [llama/dense.rs] module doc),
+ * but either all three matrices are tiled or none is. */
 typedef struct ffnq_ffn {
     ffnq_qmat gate, up, down;
 } ffnq_ffn;
@@ -215,8 +245,9 @@ FFNQ_API int ffnq_moe_route(const float* logits, const float* expert_scale, int 
  *       for r = 0..k-1:  acc += topk_w[t*k+r] * (down_e @ act_{t*k+r})[i]
  *   tail: resid[t][i] = bf16(resid[t][i] + acc)   (one raw residual add, no norm)
  * experts:   stacked [n_experts] INT4-affine gate/up [moe_inter][hidden] and
- *            down [hidden][moe_inter]; other formats are refused (UNSUPPORTED),
- *            as the pages refuse non-Affine blobs for the batched pass.
+ *            down [hidden][moe_inter], all row-major or all tiled; other
+ *            formats are refused (UNSUPPORTED), as the pages refuse non-Affine
+ *            blobs for the batched pass.
  * x:         device bf16 [m][hidden]; must not overlap resid.
  * topk_ids, topk_w, plan: as written by ffnq_moe_route for the same m, k.
  * seed:      device bf16 [m][hidden] (the gated shared expert) or NULL.
@@ -229,6 +260,20 @@ FFNQ_API int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int
                             const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
                             const uint16_t* seed, uint16_t* resid,
                             void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* ---- ffnq_packed_bytes / ffnq_pack -----------------------------------------
+ * Bytes of one n x k matrix (one expert) in a tiled format; fmt may name the
+ * row-major format or its tiled form.  0 for an unknown format or shape.
+ *
+ * ffnq_pack rearranges `src` (row-major INT8_ROW or INT4_AFFINE_G64,
+ * n_experts stacked as described at ffnq_qmat) into its tiled form at `dst`
+ * (device, 16-byte aligned, at least n_experts * ffnq_packed_bytes(...)
+ * bytes given in dst_bytes; must not overlap src).  Asynchronous on `stream`;
+ * bit-exact rearrangement, no arithmetic.  Errors: INVALID (NULL pointers,
+ * shapes, alignment, overlap), UNSUPPORTED (tiled or unknown src format,
+ * INT4 with k % 128 != 0), WORKSPACE (dst_bytes too small). */
+FFNQ_API size_t ffnq_packed_bytes(int fmt, int n, int k);
+FFNQ_API int ffnq_pack(const ffnq_qmat* src, int n_experts, void* dst, size_t dst_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 FFNQ_API const char* ffnq_status_string(int status);

@@ -17,6 +17,9 @@ from .build import LIB, build  # noqa: F401
 
 FMT_INT8_ROW = 1
 FMT_INT4_AFFINE_G64 = 2
+FMT_INT8_ROW_TILED = 3
+FMT_INT4_AFFINE_G64_TILED = 4
+TILED = {FMT_INT8_ROW: FMT_INT8_ROW_TILED, FMT_INT4_AFFINE_G64: FMT_INT4_AFFINE_G64_TILED}
 ACT_SILU = 1
 ACT_GELU_TANH = 2
 TAIL_NONE = 0
@@ -27,7 +30,7 @@ TAIL_SIGMOID_GATE = 3
 OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
 EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_status_string",
-           "ffnq_set_phase_events")
+           "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
 
 
 def plan_ints(m: int, k: int) -> int:
@@ -72,6 +75,10 @@ def lib():
         L.ffnq_status_string.restype = C.c_char_p
         L.ffnq_set_phase_events.argtypes = [vp]
         L.ffnq_set_phase_events.restype = C.c_int
+        L.ffnq_packed_bytes.argtypes = [i32, i32, i32]
+        L.ffnq_packed_bytes.restype = C.c_size_t
+        L.ffnq_pack.argtypes = [C.POINTER(QMat), i32, vp, C.c_size_t, vp]
+        L.ffnq_pack.restype = C.c_int
         _lib = L
     return _lib
 
@@ -213,3 +220,22 @@ def to_device(mat: dict, device="cuda") -> dict:
             return torch.from_numpy(a.view(np.int16)).to(device)
         return torch.from_numpy(a).to(device)
     return dict(fmt=mat["fmt"], n=mat["n"], k=mat["k"], q=t(mat["q"]), s=t(mat["s"]), z=t(mat.get("z")))
+
+
+def packed_bytes(fmt: int, n: int, k: int) -> int:
+    """Bytes of one n x k matrix (one expert) in the tiled form of `fmt` (0 if unsupported)."""
+    return int(lib().ffnq_packed_bytes(fmt, n, k))
+
+
+def pack(mat: dict, n_experts: int = 1, stream=None) -> dict:
+    """Repack a row-major device matrix dict (fmt, n, k, q, s, z; n_experts
+    stacked) into the tiled format the GPU streams fastest (ffnq_pack).
+    Returns the tiled matrix dict (q = packed buffer, s = z = None)."""
+    fmt, n, k = mat["fmt"], mat["n"], mat["k"]
+    eb = packed_bytes(fmt, n, k)
+    if eb == 0:
+        raise FfnqError("ffnq_packed_bytes", -2)
+    dst = torch.empty(eb * n_experts, dtype=torch.uint8, device=mat["q"].device)
+    src = qmat(fmt, n, k, mat["q"], mat["s"], mat.get("z"))
+    _check("ffnq_pack", lib().ffnq_pack(C.byref(src), n_experts, dst.data_ptr(), dst.numel(), _stream(stream)))
+    return dict(fmt=TILED[fmt], n=n, k=k, q=dst, s=None, z=None)

@@ -15,6 +15,7 @@
 #include "qgemm.h"
 #include "route.h"
 #include "tail.h"
+#include "tiled.h"
 
 namespace {
 
@@ -39,10 +40,13 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
-int block_k(int fmt) { return fmt == FFNQ_FMT_INT4_AFFINE_G64 ? 128 : 64; }
+bool is_tiled(int f) { return f == FFNQ_FMT_INT8_ROW_TILED || f == FFNQ_FMT_INT4_AFFINE_G64_TILED; }
+bool is_int4(int f) { return f == FFNQ_FMT_INT4_AFFINE_G64 || f == FFNQ_FMT_INT4_AFFINE_G64_TILED; }
+
+int block_k(int fmt) { return is_int4(fmt) ? 128 : 64; }
 
 // library format code -> kernel format code
-int to_fmt(int f) { return f == FFNQ_FMT_INT4_AFFINE_G64 ? ffnq::FMT_INT4 : ffnq::FMT_INT8; }
+int to_fmt(int f) { return is_int4(f) ? ffnq::FMT_INT4 : ffnq::FMT_INT8; }
 int to_fmt_dev(int f) { return to_fmt(f); }
 
 // Compute units of the current device, cached per device ordinal.
@@ -63,15 +67,19 @@ int device_cus()
 
 int check_mat(const ffnq_qmat& w, bool* unsupported)
 {
-    if (w.fmt != FFNQ_FMT_INT8_ROW && w.fmt != FFNQ_FMT_INT4_AFFINE_G64) {
+    if (w.fmt != FFNQ_FMT_INT8_ROW && w.fmt != FFNQ_FMT_INT4_AFFINE_G64 && !is_tiled(w.fmt)) {
         *unsupported = true;
         return FFNQ_ERR_UNSUPPORTED;
     }
     if (w.n <= 0 || w.k <= 0 || w.k % 64 != 0) return FFNQ_ERR_INVALID;
-    if (!w.q || !w.s) return FFNQ_ERR_INVALID;
-    if (w.fmt == FFNQ_FMT_INT4_AFFINE_G64 && !w.z) return FFNQ_ERR_INVALID;
-    if (misaligned(w.q) || misaligned(w.s) || (w.z && misaligned(w.z))) return FFNQ_ERR_INVALID;
-    if (w.fmt == FFNQ_FMT_INT4_AFFINE_G64 && w.k % 128 != 0) {
+    if (!w.q) return FFNQ_ERR_INVALID;
+    if (misaligned(w.q)) return FFNQ_ERR_INVALID;
+    if (!is_tiled(w.fmt)) {
+        if (!w.s) return FFNQ_ERR_INVALID;
+        if (w.fmt == FFNQ_FMT_INT4_AFFINE_G64 && !w.z) return FFNQ_ERR_INVALID;
+        if (misaligned(w.s) || (w.z && misaligned(w.z))) return FFNQ_ERR_INVALID;
+    }
+    if (is_int4(w.fmt) && w.k % 128 != 0) {
         *unsupported = true;
         return FFNQ_ERR_UNSUPPORTED;
     }
@@ -93,7 +101,13 @@ int check_ffn(const ffnq_ffn* f, int hidden, int inter)
     if (f->down.n != hidden || f->down.k != inter) return FFNQ_ERR_INVALID;
     if (worst != FFNQ_OK) return worst;
     if (f->gate.fmt != f->up.fmt) return FFNQ_ERR_UNSUPPORTED;
+    if (is_tiled(f->gate.fmt) != is_tiled(f->down.fmt)) return FFNQ_ERR_UNSUPPORTED;
     return FFNQ_OK;
+}
+
+long long tiled_expert_bytes(const ffnq_qmat& w)
+{
+    return tile_geo(to_fmt(w.fmt), w.n, w.k).expert_bytes;
 }
 
 MatDev mat_dev(const ffnq_qmat& w)
@@ -123,6 +137,7 @@ constexpr int kKSMax = 8;          // waves per workgroup (upper bound used for 
 struct KConfig {
     int nt, mt, ks, rows_cap, kg;
     size_t lds;
+    int grid;   // tiled kernels: workgroups along x
 };
 
 KConfig gu_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
@@ -221,6 +236,126 @@ bool launch_down(int fmt, const KConfig& c, long long items, int N, hipStream_t 
 }
 
 // ---------------------------------------------------------------------------
+// tiled kernels: configuration and dispatch
+
+// Waves per workgroup splitting a tile's K units (scale/zero groups or
+// blocks): enough waves in flight per CU (about `per_cu`) while every wave
+// keeps the smallest possible number of units, all waves equal if possible.
+int tiled_ks(int units, long long tiles_total, int cus, int per_cu, int max_ks)
+{
+    long long want = ((long long)cus * per_cu + tiles_total - 1) / std::max<long long>(1, tiles_total);
+    int ks = (int)std::max<long long>(1, std::min<long long>({want, (long long)units, (long long)max_ks}));
+    const int per = (units + ks - 1) / ks;
+    return (units + per - 1) / per;
+}
+
+KConfig gu_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+{
+    KConfig c{};
+    const int F = to_fmt(fmt);
+    const TileGeo geo = tile_geo(F, N, K);
+    const int nun = is_int4(fmt) ? geo.ng : geo.nbk;
+    const int rp = std::max(1, std::min(rows_total, 32));
+    c.nt = rp <= 16 ? 1 : 2;
+    c.mt = c.nt == 2 ? 4 : (rp <= 1 ? 1 : (rp <= 2 ? 2 : 4));
+    c.rows_cap = std::min(rp, 16 * c.nt);
+    c.kg = 1;
+    const int max_units_per_wave_int8 = 4;   // INT8: at least this many blocks per wave
+    c.ks = is_int4(fmt) ? tiled_ks(nun, items_est * geo.T, cus, 8, 8)
+                        : tiled_ks(std::max(1, nun / max_units_per_wave_int8), items_est * geo.T, cus, 8, 8);
+    for (;;) {
+        c.lds = tiled_launch_lds(2, F, N, K, 1, c.rows_cap, c.ks, 2 * c.nt * 4).total;
+        if (c.lds <= kLdsBudget || c.rows_cap <= 1) break;
+        --c.rows_cap;
+    }
+    c.grid = (int)std::max<long long>(1, std::min<long long>(items_est * geo.T, (long long)cus * 16));
+    return c;
+}
+
+// K split of the tiled down projection (device independent, so that the
+// workspace size is too): K ranges across workgroups (kg) and waves (ks).
+struct DSplit {
+    int kg, ks, rows_cap, nt;
+};
+
+DSplit down_tiled_split(int fmt, int K, int N, int rows_total)
+{
+    const int F = to_fmt(fmt);
+    const TileGeo geo = tile_geo(F, N, K);
+    const int nun = is_int4(fmt) ? geo.ng : geo.nbk;   // K units: scale/zero groups or blocks
+    const int r2 = 2 * std::max(1, rows_total);
+    const int rp = std::min(r2, 64);
+    DSplit d{};
+    d.nt = rp <= 16 ? 1 : (rp <= 32 ? 2 : 4);
+    d.rows_cap = std::min(rp, 16 * d.nt);
+    int kg = std::max(1, (kRefCUs + geo.T - 1) / geo.T);
+    kg = std::min(kg, nun);
+    while (kg < nun && tiled_launch_lds(1, F, N, K, kg, d.rows_cap, 8, 2 * d.nt).total > kLdsBudget) ++kg;
+    d.kg = kg;
+    const int upw = (nun + kg - 1) / kg;   // K units of the longest range
+    if (is_int4(fmt)) {
+        // fewest waves that give every wave the minimal number of groups
+        const int best = (upw + 7) / 8;
+        d.ks = std::max(1, (upw + best - 1) / best);
+    } else {
+        d.ks = std::max(1, std::min(8, upw / 4));
+    }
+    return d;
+}
+
+KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+{
+    const DSplit d = down_tiled_split(fmt, K, N, rows_total);
+    const int F = to_fmt(fmt);
+    const TileGeo geo = tile_geo(F, N, K);
+    KConfig c{};
+    c.nt = d.nt;
+    c.mt = c.nt > 1 ? 4 : (std::min(2 * std::max(1, rows_total), 64) <= 2 ? 2 : 4);
+    c.rows_cap = d.rows_cap;
+    c.kg = d.kg;
+    c.ks = d.ks;
+    c.lds = tiled_launch_lds(1, F, N, K, d.kg, c.rows_cap, c.ks, 2 * c.nt).total;
+    c.grid = (int)std::max<long long>(1, std::min<long long>(items_est * geo.T, (long long)cus * 16));
+    return c;
+}
+
+#define FFNQ_GUT_CASE(F, NT_, MT_)                                                                         \
+    if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                          \
+        hipExtLaunchKernelGGL((gu_tiled_kernel<F, NT_, MT_>), dim3(c.grid), dim3(64 * c.ks), c.lds, stream, \
+                              phase_event(0), phase_event(1), 0, prm);                                     \
+        return true;                                                                                       \
+    }
+
+bool launch_gu_tiled(int fmt, const KConfig& c, hipStream_t stream, const GUParams& prm)
+{
+    FFNQ_GUT_CASE(FMT_INT4, 1, 1) FFNQ_GUT_CASE(FMT_INT4, 1, 2) FFNQ_GUT_CASE(FMT_INT4, 1, 4)
+    FFNQ_GUT_CASE(FMT_INT4, 2, 4) FFNQ_GUT_CASE(FMT_INT8, 1, 1) FFNQ_GUT_CASE(FMT_INT8, 1, 2)
+    FFNQ_GUT_CASE(FMT_INT8, 1, 4) FFNQ_GUT_CASE(FMT_INT8, 2, 4)
+    return false;
+}
+
+#define FFNQ_DNT_CASE(F, NT_, MT_)                                                                           \
+    if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                            \
+        hipExtLaunchKernelGGL((down_tiled_kernel<F, NT_, MT_>), dim3(c.grid, c.kg), dim3(64 * c.ks), c.lds,   \
+                              stream, phase_event(2), phase_event(3), 0, prm);                               \
+        return true;                                                                                         \
+    }
+
+bool launch_down_tiled(int fmt, const KConfig& c, hipStream_t stream, const DownParams& prm)
+{
+    FFNQ_DNT_CASE(FMT_INT4, 1, 2) FFNQ_DNT_CASE(FMT_INT4, 1, 4) FFNQ_DNT_CASE(FMT_INT4, 2, 4)
+    FFNQ_DNT_CASE(FMT_INT4, 4, 4) FFNQ_DNT_CASE(FMT_INT8, 1, 2) FFNQ_DNT_CASE(FMT_INT8, 1, 4)
+    FFNQ_DNT_CASE(FMT_INT8, 2, 4) FFNQ_DNT_CASE(FMT_INT8, 4, 4)
+    return false;
+}
+
+// K ranges of the down projection for a format (row-major or tiled).
+int down_ranges(int fmt, int K, int N, int rows_total)
+{
+    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total).kg : down_kg(fmt, K, N, rows_total);
+}
+
+// ---------------------------------------------------------------------------
 // dense FFN (ffnq_dense and ffnq_shared_expert)
 
 struct DenseWs {
@@ -231,7 +366,7 @@ DenseWs dense_ws(int fmt_down, int hidden, int inter, int m)
 {
     DenseWs w{};
     size_t o = 0;
-    const int kg = down_kg(fmt_down, inter, hidden, m);
+    const int kg = down_ranges(fmt_down, inter, hidden, m);
     w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * m * hidden * sizeof(float), 256);
     w.logit = o; o += align_up((size_t)m * sizeof(float), 256);
@@ -247,7 +382,9 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
     const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m);
     const int gfmt = to_fmt(ffn->gate.fmt), dfmt = to_fmt(ffn->down.fmt);
 
-    const KConfig gc = gu_config(ffn->gate.fmt, hidden, inter, 1, m, cus);
+    const bool tiled = is_tiled(ffn->gate.fmt);
+    const KConfig gc = tiled ? gu_tiled_config(ffn->gate.fmt, hidden, inter, 1, m, cus)
+                             : gu_config(ffn->gate.fmt, hidden, inter, 1, m, cus);
     GUParams gp{};
     gp.gate = mat_dev(ffn->gate);
     gp.up = mat_dev(ffn->up);
@@ -265,10 +402,18 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
         gp.gate_vec = aux;
         gp.logit = reinterpret_cast<float*>(base + L.logit);
     }
-    if (!launch_gu(gfmt, gc, 1, inter, stream, gp)) return FFNQ_ERR_UNSUPPORTED;
+    if (tiled) {
+        gp.tgate = static_cast<const uint8_t*>(ffn->gate.q);
+        gp.tup = static_cast<const uint8_t*>(ffn->up.q);
+        gp.tebytes = tiled_expert_bytes(ffn->gate);
+        gp.dfmt = FMT_NATURAL;   // a tiled down matrix reads the activation in natural order
+    }
+    if (!(tiled ? launch_gu_tiled(gfmt, gc, stream, gp) : launch_gu(gfmt, gc, 1, inter, stream, gp)))
+        return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    const KConfig dc = down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
+    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus)
+                             : down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
     DownParams dp{};
     dp.down = mat_dev(ffn->down);
     dp.N = hidden;
@@ -288,7 +433,12 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
         case FFNQ_TAIL_SIGMOID_GATE: dp.tail = TAIL_SIGMOID; break;
         default: dp.tail = TAIL_NONE; break;
     }
-    if (!launch_down(dfmt, dc, 1, hidden, stream, dp)) return FFNQ_ERR_UNSUPPORTED;
+    if (tiled) {
+        dp.tdown = static_cast<const uint8_t*>(ffn->down.q);
+        dp.tebytes = tiled_expert_bytes(ffn->down);
+    }
+    if (!(tiled ? launch_down_tiled(dfmt, dc, stream, dp) : launch_down(dfmt, dc, 1, hidden, stream, dp)))
+        return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     if (tail == FFNQ_TAIL_RMSNORM) {
@@ -345,11 +495,11 @@ struct RoutedWs {
     size_t act, part, total;
 };
 
-RoutedWs routed_ws(int hidden, int moe_inter, int m, int k)
+RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k)
 {
     RoutedWs w{};
     const size_t P = (size_t)m * k;
-    const int kg = down_kg(FFNQ_FMT_INT4_AFFINE_G64, moe_inter, hidden, m);
+    const int kg = down_ranges(fmt, moe_inter, hidden, m);
     size_t o = 0;
     w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
@@ -372,6 +522,48 @@ const char* ffnq_status_string(int status)
         case FFNQ_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }
+}
+
+size_t ffnq_packed_bytes(int fmt, int n, int k)
+{
+    if (fmt != FFNQ_FMT_INT8_ROW && fmt != FFNQ_FMT_INT4_AFFINE_G64 && !is_tiled(fmt)) return 0;
+    if (n <= 0 || k <= 0 || k % 64 != 0 || (is_int4(fmt) && k % 128 != 0)) return 0;
+    return (size_t)tile_geo(to_fmt(fmt), n, k).expert_bytes;
+}
+
+int ffnq_pack(const ffnq_qmat* src, int n_experts, void* dst, size_t dst_bytes, hipStream_t stream)
+{
+    if (!src || !dst || n_experts <= 0) return FFNQ_ERR_INVALID;
+    if (src->fmt != FFNQ_FMT_INT8_ROW && src->fmt != FFNQ_FMT_INT4_AFFINE_G64) return FFNQ_ERR_UNSUPPORTED;
+    bool uns = false;
+    const int rc = check_mat(*src, &uns);
+    if (rc != FFNQ_OK) return rc;
+    if (misaligned(dst)) return FFNQ_ERR_INVALID;
+    const long long eb = tile_geo(to_fmt(src->fmt), src->n, src->k).expert_bytes;
+    if ((long long)n_experts > (1LL << 40) / eb) return FFNQ_ERR_INVALID;
+    const size_t need = (size_t)eb * (size_t)n_experts;
+    if (dst_bytes < need) return FFNQ_ERR_WORKSPACE;
+    const MatDev d = mat_dev(*src);
+    const size_t qbytes = (size_t)d.qe * n_experts;
+    const size_t sbytes = (size_t)d.se * n_experts * (is_int4(src->fmt) ? 2 : 4);
+    if (overlap(dst, need, src->q, qbytes) || overlap(dst, need, src->s, sbytes) ||
+        (src->z && overlap(dst, need, src->z, sbytes)))
+        return FFNQ_ERR_INVALID;
+    PackParams p{};
+    p.fmt = to_fmt(src->fmt);
+    p.n = src->n;
+    p.k = src->k;
+    p.n_experts = n_experts;
+    p.q = static_cast<const uint8_t*>(src->q);
+    p.s = src->s;
+    p.z = static_cast<const uint16_t*>(src->z);
+    p.qe = d.qe;
+    p.se = d.se;
+    p.dst = static_cast<uint8_t*>(dst);
+    const long long chunks = (long long)need / 16;
+    const int grid = (int)std::min<long long>((chunks + 255) / 256, (long long)device_cus() * 16);
+    hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
 }
 
 int ffnq_set_phase_events(hipEvent_t* ev)
@@ -421,8 +613,7 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
     const int rc = check_ffn(experts, hidden, moe_inter);
     if (rc != FFNQ_OK) return rc;
-    if (experts->gate.fmt != FFNQ_FMT_INT4_AFFINE_G64 || experts->up.fmt != FFNQ_FMT_INT4_AFFINE_G64 ||
-        experts->down.fmt != FFNQ_FMT_INT4_AFFINE_G64)
+    if (!is_int4(experts->gate.fmt) || !is_int4(experts->up.fmt) || !is_int4(experts->down.fmt))
         return FFNQ_ERR_UNSUPPORTED;
     if (act != FFNQ_ACT_SILU && act != FFNQ_ACT_GELU_TANH) return FFNQ_ERR_UNSUPPORTED;
     if (!x || !topk_ids || !topk_w || !plan || !resid) return FFNQ_ERR_INVALID;
@@ -432,7 +623,7 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
     const size_t rows_bytes = (size_t)m * hidden * 2;
     if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
-    const RoutedWs L = routed_ws(hidden, moe_inter, m, top_k);
+    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k);
     if (!ws) {
         *ws_bytes = L.total;
         return FFNQ_OK;
@@ -447,7 +638,9 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     const long long u_est = std::min<long long>(P, n_experts);
 
     // phase 1: gate/up + activation per union entry and tile
-    const KConfig gc = gu_config(FFNQ_FMT_INT4_AFFINE_G64, hidden, moe_inter, u_est, m, cus);
+    const bool tiled = is_tiled(experts->gate.fmt);
+    const KConfig gc = tiled ? gu_tiled_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus)
+                             : gu_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus);
     GUParams gp{};
     gp.gate = mat_dev(experts->gate);
     gp.up = mat_dev(experts->up);
@@ -464,11 +657,19 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     gp.n_experts = n_experts;
     gp.act_out = reinterpret_cast<uint16_t*>(base + L.act);
     gp.act_rows = P;
-    if (!launch_gu(FMT_INT4, gc, u_est, moe_inter, stream, gp)) return FFNQ_ERR_UNSUPPORTED;
+    if (tiled) {
+        gp.tgate = static_cast<const uint8_t*>(experts->gate.q);
+        gp.tup = static_cast<const uint8_t*>(experts->up.q);
+        gp.tebytes = tiled_expert_bytes(experts->gate);
+        gp.dfmt = FMT_NATURAL;
+    }
+    if (!(tiled ? launch_gu_tiled(FMT_INT4, gc, stream, gp) : launch_gu(FMT_INT4, gc, u_est, moe_inter, stream, gp)))
+        return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     // phase 2: down per union entry and tile, d_p to pair_out
-    const KConfig dc = down_config(FFNQ_FMT_INT4_AFFINE_G64, moe_inter, hidden, u_est, m, cus);
+    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus)
+                             : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
     DownParams dp{};
     dp.down = mat_dev(experts->down);
     dp.N = hidden;
@@ -484,7 +685,12 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     dp.n_experts = n_experts;
     dp.tail = TAIL_PAIR;
     dp.part = reinterpret_cast<float*>(base + L.part);
-    if (!launch_down(FMT_INT4, dc, u_est, hidden, stream, dp)) return FFNQ_ERR_UNSUPPORTED;
+    if (tiled) {
+        dp.tdown = static_cast<const uint8_t*>(experts->down.q);
+        dp.tebytes = tiled_expert_bytes(experts->down);
+    }
+    if (!(tiled ? launch_down_tiled(FMT_INT4, dc, stream, dp) : launch_down(FMT_INT4, dc, u_est, hidden, stream, dp)))
+        return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     // seeded rank-ordered reduce + residual

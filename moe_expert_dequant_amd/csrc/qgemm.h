@@ -22,7 +22,7 @@
 
 namespace ffnq {
 
-enum { FMT_INT8 = 1, FMT_INT4 = 2 };
+enum { FMT_NATURAL = 0, FMT_INT8 = 1, FMT_INT4 = 2 };
 
 template <int FMT>
 struct FmtT;
@@ -78,10 +78,12 @@ __device__ __forceinline__ int cons_pos<FMT_INT8>(int r)
     return (4 * ((r >> 3) & 1) + (r >> 4)) * 8 + (r & 7);
 }
 
+// dfmt 0 (FMT_NATURAL): the tiled formats consume activations in natural order.
 __device__ __forceinline__ int cons_index(int dfmt, int k)
 {
     if (dfmt == FMT_INT4) return (k & ~127) + cons_pos<FMT_INT4>(k & 127);
-    return (k & ~63) + cons_pos<FMT_INT8>(k & 63);
+    if (dfmt == FMT_INT8) return (k & ~63) + cons_pos<FMT_INT8>(k & 63);
+    return k;
 }
 
 // --------------------------------------------------------------------------
@@ -481,6 +483,9 @@ struct GUParams {
     int act_rows;              // m, or m*top_k
     const uint16_t* gate_vec;  // dense shared-expert gate: logit[t] = <gate_vec, x_t>
     float* logit;
+    const uint8_t* tgate;      // tiled formats: packed gate / up (expert 0)
+    const uint8_t* tup;
+    long long tebytes;         // tiled bytes per expert
 };
 
 template <int FMT, int NT, int MT>
@@ -622,6 +627,8 @@ struct DownParams {
     uint16_t* out;             // [m][N] bf16
     float* part;               // [KG][rows][N] fp32 partial h (rows: m tokens or act_rows pairs)
     const float* logit;        // [m] (SIGMOID)
+    const uint8_t* tdown;      // tiled formats: packed down (expert 0)
+    long long tebytes;         // tiled bytes per expert
 };
 
 __device__ __forceinline__ void down_finish(const DownParams& p, int t, int n, float h)

@@ -167,3 +167,59 @@ def test_routed_refusals_and_query():
     assert call_routed(f, plan=None)[0] == -1
     assert call_routed(f, resid=addr(40) + 64)[0] == -1       # overlaps x
     assert call_routed(f, ws=addr(60), ws_bytes=n - 256)[0] == -4
+
+
+# ---------------------------------------------------------------------------
+# tiled formats and ffnq_pack (refusals only: no launch)
+
+T8, T4 = fq.FMT_INT8_ROW_TILED, fq.FMT_INT4_AFFINE_G64_TILED
+
+
+def test_packed_bytes():
+    # INT4 4096 inputs: 32 code blocks in 4 groups -> 36 KB per 16-row tile; no padding at 14336 rows
+    assert fq.packed_bytes(I4, 14336, 4096) == 896 * 36 * 1024 == 14336 * 2048 + 4 * 14336 * 4096 // 64
+    assert fq.packed_bytes(T4, 14336, 4096) == fq.packed_bytes(I4, 14336, 4096)
+    # short last group (6 blocks) and a ragged tile: 2 tiles of (1 + 6) steps
+    assert fq.packed_bytes(I4, 20, 768) == 2 * 7 * 1024
+    # INT8: 16-row tiles of K/64 steps, then 16 fp32 scales per tile padded to 256 bytes
+    assert fq.packed_bytes(I8, 37, 320) == 3 * 5 * 1024 + 256
+    assert fq.packed_bytes(I8, 2816, 11264) == 176 * 176 * 1024 + 176 * 64
+    for bad in ((I4, 16, 192), (I8, 16, 100), (I4, 0, 128), (99, 16, 128), (I8, 16, -64)):
+        assert fq.packed_bytes(*bad) == 0, bad
+
+
+def test_pack_refusals():
+    L = fq.lib()
+    src = mat(I4, 32, 256, 0)
+    need = fq.packed_bytes(I4, 32, 256)
+    assert L.ffnq_pack(None, 1, addr(100), need, None) == -1
+    assert L.ffnq_pack(C.byref(src), 0, addr(100), need, None) == -1
+    assert L.ffnq_pack(C.byref(src), 1, None, need, None) == -1
+    assert L.ffnq_pack(C.byref(src), 1, addr(100), need - 16, None) == -4
+    assert L.ffnq_pack(C.byref(src), 2, addr(100), need, None) == -4
+    assert L.ffnq_pack(C.byref(src), 1, addr(100) + 8, need, None) == -1          # misaligned dst
+    assert L.ffnq_pack(C.byref(src), 1, addr(0), need, None) == -1                # dst overlaps src codes
+    tiled = fq.QMat(T4, 32, 256, addr(0), None, None)
+    assert L.ffnq_pack(C.byref(tiled), 1, addr(100), need, None) == -2            # already tiled
+    odd = mat(I4, 32, 192, 0)
+    assert L.ffnq_pack(C.byref(odd), 1, addr(100), need, None) == -2             # k % 128 != 0
+
+
+def tiled_ffn(fmt_gu, fmt_d, hidden, inter):
+    return fq.Ffn(fq.QMat(fmt_gu, inter, hidden, addr(0), None, None),
+                  fq.QMat(fmt_gu, inter, hidden, addr(10), None, None),
+                  fq.QMat(fmt_d, hidden, inter, addr(20), None, None))
+
+
+def test_tiled_ffn_checks():
+    rc, n = call_dense(tiled_ffn(T4, T4, 256, 512))
+    assert rc == 0 and n > 0                                  # workspace query accepts tiled weights
+    rc, _ = call_dense(tiled_ffn(T4, T8, 256, 512))
+    assert rc == 0                                            # mixed tiled formats are fine
+    mixed = fq.Ffn(fq.QMat(T4, 512, 256, addr(0), None, None), fq.QMat(T4, 512, 256, addr(10), None, None),
+                   mat(I4, 256, 512, 20))
+    rc, _ = call_dense(mixed)
+    assert rc == -2                                           # tiled and row-major mixed: refused
+    rc, _ = call_dense(fq.Ffn(fq.QMat(T4, 512, 256, None, None, None), fq.QMat(T4, 512, 256, addr(10), None, None),
+                              fq.QMat(T4, 256, 512, addr(20), None, None)))
+    assert rc == -1                                           # NULL packed buffer

@@ -36,8 +36,19 @@ def host16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def ffn_dev(f):
+LAYOUTS = pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
+
+
+def mats_dev(f, tiled=False, n_experts=1):
+    """Device copies of an FFN's matrices; tiled=True repacks them with ffnq_pack."""
     d = {n: fq.to_device(f[n]) for n in ("gate", "up", "down")}
+    if tiled:
+        d = {n: fq.pack(d[n], n_experts) for n in d}
+    return d
+
+
+def ffn_dev(f, tiled=False):
+    d = mats_dev(f, tiled)
     return d, fq.ffn_struct(d)
 
 
@@ -50,8 +61,8 @@ def ulp_diag(got, want):
     return float(np.max(np.abs(g - w) / ulp)), float(np.max(np.abs(g - w)))
 
 
-def gpu_dense(inp, hidden, inter, act, tail, shared=False, aux=None, eps=1e-6):
-    d, st = ffn_dev(inp["ffn"])
+def gpu_dense(inp, hidden, inter, act, tail, shared=False, aux=None, eps=1e-6, tiled=False):
+    d, st = ffn_dev(inp["ffn"], tiled)
     x = dev16(inp["x"])
     m = inp["x"].shape[0]
     if shared:
@@ -83,55 +94,59 @@ DENSE_CASES = [(fg, fd, act, tail, m)
                for m in (1, 3, 17)]
 
 
+@LAYOUTS
 @pytest.mark.parametrize("fg,fd,act,tail,m", DENSE_CASES)
-def test_dense_small(fg, fd, act, tail, m):
+def test_dense_small(fg, fd, act, tail, m, tiled):
     hidden, inter = 512, 768
-    say("dense_small", fg, fd, act, tail, m)
+    say("dense_small", fg, fd, act, tail, m, "tiled" if tiled else "rowmajor")
     inp = gen.dense_inputs(hidden, inter, m, fg, seed=1000 + 10 * fg + fd + 100 * m, fmt_down=fd)
     aux = inp["norm_w"] if tail == gen.TAIL_RMSNORM else None
     want = oracle.dense(inp["ffn"], hidden, inter, act, tail, inp["x"],
                         inp["resid"] if tail == gen.TAIL_RESIDUAL else None, aux)
-    got = gpu_dense(inp, hidden, inter, act, tail, aux=aux)
-    check(got, want, f"dense fmt {fg}/{fd} act {act} tail {tail} m {m}")
+    got = gpu_dense(inp, hidden, inter, act, tail, aux=aux, tiled=tiled)
+    check(got, want, f"dense fmt {fg}/{fd} act {act} tail {tail} m {m} tiled {tiled}")
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 33])
 @pytest.mark.parametrize("tail", [gen.TAIL_NONE, gen.TAIL_RMSNORM, gen.TAIL_SIGMOID_GATE])
-def test_shared_expert_small(tail, m):
+def test_shared_expert_small(tail, m, tiled):
     hidden, inter = 384, 640
-    say("shared_small", tail, m)
+    say("shared_small", tail, m, tiled)
     inp = gen.dense_inputs(hidden, inter, m, I8, seed=2000 + m + 7 * tail)
     aux = {gen.TAIL_NONE: None, gen.TAIL_RMSNORM: inp["norm_w"], gen.TAIL_SIGMOID_GATE: inp["gate_vec"]}[tail]
     want = oracle.shared_expert(inp["ffn"], hidden, inter, gen.ACT_GELU_TANH, tail, inp["x"], aux)
-    got = gpu_dense(inp, hidden, inter, gen.ACT_GELU_TANH, tail, shared=True, aux=aux)
-    check(got, want, f"shared tail {tail} m {m}")
+    got = gpu_dense(inp, hidden, inter, gen.ACT_GELU_TANH, tail, shared=True, aux=aux, tiled=tiled)
+    check(got, want, f"shared tail {tail} m {m} tiled {tiled}")
 
 
+@LAYOUTS
 @pytest.mark.parametrize("fmt", [I8, I4])
 @pytest.mark.parametrize("act", [gen.ACT_SILU, gen.ACT_GELU_TANH])
 @pytest.mark.parametrize("m", [1, 4, 9])
-def test_integer_regime_bit_exact(fmt, act, m):
+def test_integer_regime_bit_exact(fmt, act, m, tiled):
     hidden, inter = 256, 384
-    say("integer_regime", fmt, act, m)
+    say("integer_regime", fmt, act, m, tiled)
     ffn, x, resid, h, rv = integer_regime(fmt, hidden, inter, m, 300 + fmt + m)
     want = oracle.dense(ffn, hidden, inter, act, gen.TAIL_RESIDUAL, x, resid)
-    got = gpu_dense(dict(ffn=ffn, x=x, resid=resid), hidden, inter, act, gen.TAIL_RESIDUAL)
+    got = gpu_dense(dict(ffn=ffn, x=x, resid=resid), hidden, inter, act, gen.TAIL_RESIDUAL, tiled=tiled)
     assert np.array_equal(got, want)
     want = oracle.shared_expert(ffn, hidden, inter, act, gen.TAIL_NONE, x, None)
-    got = gpu_dense(dict(ffn=ffn, x=x, resid=resid), hidden, inter, act, gen.TAIL_NONE, shared=True)
+    got = gpu_dense(dict(ffn=ffn, x=x, resid=resid), hidden, inter, act, gen.TAIL_NONE, shared=True, tiled=tiled)
     assert np.array_equal(got, want)
 
 
-def test_zero_input_and_repeat_calls():
+@LAYOUTS
+def test_zero_input_and_repeat_calls(tiled):
     hidden, inter = 512, 768
     inp = gen.dense_inputs(hidden, inter, 3, I4, seed=77)
     inp["x"] = np.zeros_like(inp["x"])
-    got = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL)
+    got = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, tiled=tiled)
     assert np.array_equal(got, inp["resid"])
-    # the same call twice (workspace counters are reset within each call)
+    # the same call twice gives the same bits
     inp = gen.dense_inputs(hidden, inter, 3, I4, seed=78)
-    a = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL)
-    b = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL)
+    a = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, tiled=tiled)
+    b = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, tiled=tiled)
     assert np.array_equal(a, b)
 
 
@@ -197,14 +212,15 @@ def gpu_routed(ex_dev, ex_struct, E, hidden, inter, k, cap, inp, seed_bits, act=
     return host16(resid), ids, w
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m,k,cap,use_seed", [(1, 4, 8, True), (3, 4, 8, True), (8, 4, 8, True), (8, 4, 8, False),
                                               (20, 2, 16, True), (5, 6, 6, False)])
-def test_routed_small(m, k, cap, use_seed):
+def test_routed_small(m, k, cap, use_seed, tiled):
     hidden, inter, E = 512, 256, 16
-    say("routed_small", m, k, cap, use_seed)
+    say("routed_small", m, k, cap, use_seed, tiled)
     inp = gen.moe_inputs(hidden, E, inter, m, seed=3000 + m + 10 * k)
     seed_bits = gen.act_rows(gen.tensor_key(3100, m), m, hidden) if use_seed else None
-    d = {n: fq.to_device(inp["experts"][n]) for n in ("gate", "up", "down")}
+    d = mats_dev(inp["experts"], tiled, E)
     got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, cap, inp, seed_bits)
     want = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids, w, seed_bits,
                              inp["resid"])
@@ -215,45 +231,49 @@ def test_routed_small(m, k, cap, use_seed):
 # full-size workloads (sampled where the oracle would be slow)
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m", [1, 4])
-def test_config0_dense_int8(m):
+def test_config0_dense_int8(m, tiled):
     c = gen.CONFIGS[0]
-    say("config0", m)
+    say("config0", m, tiled)
     inp = gen.config_inputs(0, m)
     want = oracle.dense(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"], inp["resid"])
-    got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"])
-    check(got, want, f"config0 m {m}")
+    got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], tiled=tiled)
+    check(got, want, f"config0 m {m} tiled {tiled}")
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m", [1, 4])
-def test_config1_llama_int4(m):
+def test_config1_llama_int4(m, tiled):
     c = gen.CONFIGS[1]
-    say("config1", m)
+    say("config1", m, tiled)
     inp = gen.config_inputs(1, m)
-    got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"])
+    got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], tiled=tiled)
     want = oracle.dense(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"], inp["resid"])
     check(got, want, f"config1 m {m}")
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m", [1, 8])
-def test_config2_gemma_shared(m):
+def test_config2_gemma_shared(m, tiled):
     c = gen.CONFIGS[2]
-    say("config2", m)
+    say("config2", m, tiled)
     inp = gen.config_inputs(2, m)
-    got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], shared=True, aux=inp["norm_w"])
+    got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], shared=True, aux=inp["norm_w"], tiled=tiled)
     rows = list(range(m)) if m <= 2 else [0, m // 2, m - 1]
     want = oracle.shared_expert(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"][rows],
                                 inp["norm_w"], c["eps"])
     check(got[rows], want, f"config2 m {m}")
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m", [1, 2, 4])
-def test_config3_qwen_moe(m):
+def test_config3_qwen_moe(m, tiled):
     c = gen.CONFIGS[3]
-    say("config3", m)
+    say("config3", m, tiled)
     inp = gen.config_inputs(3, m)
     hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
-    sh_d, sh_st = ffn_dev(inp["shared"])
+    sh_d, sh_st = ffn_dev(inp["shared"], tiled)
     seed = torch.zeros((m, hidden), dtype=torch.int16, device="cuda")
     fq.shared_expert(sh_st, hidden, c["shared_inter"], m, c["act"], gen.TAIL_SIGMOID_GATE, dev16(inp["x"]), seed,
                      dev16(inp["gate_vec"]))
@@ -262,7 +282,7 @@ def test_config3_qwen_moe(m):
     want_seed = oracle.shared_expert(inp["shared"], hidden, c["shared_inter"], c["act"], gen.TAIL_SIGMOID_GATE,
                                      inp["x"], inp["gate_vec"])
     check(seed_bits, want_seed, f"config3 shared m {m}")
-    d = {n: fq.to_device(inp["experts"][n]) for n in ("gate", "up", "down")}
+    d = mats_dev(inp["experts"], tiled, E)
     got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, c["cap"], inp, seed_bits)
     # the routed half is checked on the GPU's own seed, so its error is the routed half's alone
     want = oracle.moe_routed(inp["experts"], E, hidden, inter, c["act"], inp["x"], ids, w, seed_bits, inp["resid"])
@@ -271,13 +291,14 @@ def test_config3_qwen_moe(m):
     assert np.array_equal(ids, ids_o)
 
 
+@LAYOUTS
 @pytest.mark.parametrize("m", [1, 64])
-def test_config4_mixtral_moe(m):
+def test_config4_mixtral_moe(m, tiled):
     c = gen.CONFIGS[4]
-    say("config4", m)
+    say("config4", m, tiled)
     inp = gen.config_inputs(4, m)
     hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
-    d = {n: fq.to_device(inp["experts"][n]) for n in ("gate", "up", "down")}
+    d = mats_dev(inp["experts"], tiled, E)
     got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, c["cap"], inp, None)
     rows = list(range(m)) if m <= 2 else [0, 21, 42, 63]
     want = oracle.moe_routed(inp["experts"], E, hidden, inter, c["act"], inp["x"][rows], ids[rows], w[rows], None,
