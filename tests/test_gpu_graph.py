@@ -1,0 +1,73 @@
+"""HIP-graph capture of the library's calls: a captured dense call and a
+captured route + routed call are replayed several times, with eager work and
+synchronisation between the replays, and every replay must equal the eager
+result bit for bit (the calls enqueue only kernels: no memset or copy nodes)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import moe_expert_dequant_amd as fq
+from test_gpu_parity import LAYOUTS, dev, dev16, ffn_dev, mats_dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+@LAYOUTS
+def test_graph_replay_dense(tiled):
+    hidden, inter, m = 512, 768, 3
+    say("graph dense", tiled)
+    inp = gen.dense_inputs(hidden, inter, m, gen.FMT_INT4_AFFINE_G64, seed=4242)
+    d, st = ffn_dev(inp["ffn"], tiled)
+    x, r0 = dev16(inp["x"]), dev16(inp["resid"])
+    ws = fq.Workspace()
+    want = r0.clone()
+    fq.dense(st, hidden, inter, m, gen.ACT_SILU, gen.TAIL_RESIDUAL, x, want, ws=ws)
+    torch.cuda.synchronize()
+    r = r0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fq.dense(st, hidden, inter, m, gen.ACT_SILU, gen.TAIL_RESIDUAL, x, r, ws=ws)
+    other = r0.clone()
+    for rep in range(4):
+        r.copy_(r0)
+        fq.dense(st, hidden, inter, m, gen.ACT_SILU, gen.TAIL_RESIDUAL, x, other, ws=fq.Workspace())   # eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r, want), rep
+
+
+@LAYOUTS
+def test_graph_replay_routed(tiled):
+    hidden, inter, E, m, k, cap = 512, 256, 16, 5, 4, 8
+    say("graph routed", tiled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4343)
+    d = mats_dev(inp["experts"], tiled, E)
+    st = fq.ffn_struct(d)
+    x, r0, lg = dev16(inp["x"]), dev16(inp["resid"]), dev(inp["logits"].astype(np.float32))
+    seed = dev16(gen.act_rows(gen.tensor_key(4344, m), m, hidden))
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    ws = fq.Workspace()
+
+    def layer(resid):
+        fq.moe_route(lg, m, E, k, cap, ids, w, plan)
+        fq.moe_routed_batched(st, E, hidden, inter, m, k, gen.ACT_SILU, x, ids, w, plan, seed, resid, ws=ws)
+
+    want = r0.clone()
+    layer(want)
+    torch.cuda.synchronize()
+    r = r0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(r)
+    for rep in range(4):
+        r.copy_(r0)
+        ids.fill_(-7)
+        plan.fill_(-7)                      # eager work that the replay must overwrite
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r, want), rep
