@@ -108,6 +108,15 @@ __device__ __forceinline__ void split_bf16(float a, uint16_t& hi, uint16_t& lo)
     lo = bf16_rne(a - bf16_f32(hi));
 }
 
+// The gated activation in fp32 (device exp/tanh).  For g >= 24 both forms
+// return g exactly (exp(-g) and 1 - tanh are below half an ulp of 1).
+__device__ __forceinline__ float act_f32(int act, float g)
+{
+    if (act == 1) return g / (1.0f + __expf(-g));
+    const float c = 0.7978845608028654f;   // sqrt(2/pi)
+    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+}
+
 __device__ __forceinline__ double act_f64(int act, double g)
 {
     if (act == 1) return g / (1.0 + exp(-g));

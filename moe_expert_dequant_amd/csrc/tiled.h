@@ -218,68 +218,136 @@ __device__ __forceinline__ float tile_row_scale(const uint8_t* p, int lr)
 }
 
 // --------------------------------------------------------------------------
+// Staging of activation rows 0..Rc-1, blocks [kb0, kb0+nbk), into the
+// swizzled slot layout (slot r*per_row + (j ^ s(r)) holds piece j of row r),
+// with coalesced 16-byte loads through registers.  Pieces are handed out in
+// batches of kSR per thread; every batch issues all of its loads before its
+// stores, and the last batch's stores are deferred to finish(), so that the
+// caller can issue the weight ring in between and one wait covers both.
+constexpr int kSR = 8;
+
+template <int FMT>
+struct RegStager {
+    const Lds& L;
+    const uint16_t* src;
+    int Rc, kb0, xslots;
+    u32x4 v[kSR];
+    int slot[kSR];
+
+    __device__ __forceinline__ RegStager(const Lds& l, const uint16_t* s, int rc, int k0)
+        : L(l), src(s), Rc(rc), kb0(k0), xslots(rc * l.per_row) {}
+
+    __device__ __forceinline__ void load(int base)
+    {
+        constexpr int BK = FmtT<FMT>::BK, CPB = BK / 8;
+        const int per_row = L.per_row;
+#pragma unroll
+        for (int i = 0; i < kSR; ++i) {
+            const int sl = min(base + (int)threadIdx.x + i * (int)blockDim.x, xslots - 1);
+            const int rr = sl / per_row, jp = sl - rr * per_row;
+            const int lb = jp / CPB, ci = (jp - lb * CPB) ^ ((rr >> L.swz_shift) & L.swz_mask);
+            v[i] = *(const u32x4*)(src + L.roff[rr] + (kb0 + lb) * BK + ci * 8);
+            slot[i] = sl;
+        }
+    }
+    __device__ __forceinline__ void store()
+    {
+#pragma unroll
+        for (int i = 0; i < kSR; ++i) *(u32x4*)(L.x + (size_t)slot[i] * 16) = v[i];
+    }
+    // all batches but the last, then the last batch's loads
+    __device__ __forceinline__ void begin()
+    {
+        const int step = kSR * (int)blockDim.x;
+        int base = 0;
+        for (; base + step < xslots; base += step) {
+            load(base);
+            store();
+        }
+        load(base);
+    }
+    __device__ __forceinline__ void finish() { store(); }
+};
+
+// --------------------------------------------------------------------------
 // One code step of tiled matrices (natural input order, see the layout
-// above).  INT4 accumulates per element in `acc` (fp32 scalars, so that a
-// partial-row update does not rebuild a vector); INT8 accumulates on the MFMA
-// in `tot`/`one`.
-template <int FMT, int NMAT, int NT, int MT, typename XLoad>
-__device__ __forceinline__ void compute_step(const u32x4 (&cq)[NMAT], const uint32_t (&cs)[NMAT],
-                                             const uint32_t (&cz)[NMAT], XLoad&& xl, float (&acc)[NMAT][NT][4],
-                                             f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT])
+// above): widen() turns the ring slot's codes (and the step's scale/zero
+// pair) into MFMA operands; contract() runs the matrix-core work.  (Refilling
+// the slot between the two halves keeps more loads in flight but holds the
+// widened operands across the refill; measured, the lower occupancy costs
+// more than the overlap gains.)  INT4 accumulates per
+// element in `acc` (fp32 scalars, so that a partial-row update does not
+// rebuild a vector); INT8 accumulates on the MFMA in `tot`/`one`.
+template <int FMT, int NMAT>
+struct Widened;
+template <int NMAT>
+struct Widened<FMT_INT4, NMAT> {
+    u32x4 bw[NMAT][4];
+    float sg[NMAT][2], zg[NMAT][2];
+};
+template <int NMAT>
+struct Widened<FMT_INT8, NMAT> {
+    u32x4 bw[NMAT][2];
+};
+
+template <int FMT, int NMAT>
+__device__ __forceinline__ void widen(const u32x4 (&cq)[NMAT], const uint32_t (&cs)[NMAT], const uint32_t (&cz)[NMAT],
+                                      Widened<FMT, NMAT>& W)
 {
-    constexpr int MTC = (NT == 1) ? MT : 4;
-    constexpr int STEPS = FmtT<FMT>::STEPS;
-    const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FMT == FMT_INT4) {
-        u32x4 bw[NMAT][4];
-        float sg[NMAT][2], zg[NMAT][2];
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt) {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) bw[mt][d] = unpack_int4_biased(cq[mt][d]);
-            sg[mt][0] = bf16lo_f32(cs[mt]);
-            sg[mt][1] = bf16hi_f32(cs[mt]);
-            zg[mt][0] = bf16lo_f32(cz[mt]) + 128.0f;
-            zg[mt][1] = bf16hi_f32(cz[mt]) + 128.0f;
-        }
-#pragma unroll
-        for (int tb = 0; tb < NT; ++tb) {
-            u32x4 xs[STEPS];
-            xl(tb, xs);
-#pragma unroll
-            for (int jg = 0; jg < 2; ++jg) {
-                f32x4 o = mfma_bf16(xs[2 * jg], ones, zero);
-                o = mfma_bf16(xs[2 * jg + 1], ones, o);
-#pragma unroll
-                for (int mt = 0; mt < NMAT; ++mt) {
-                    f32x4 a = mfma_bf16(xs[2 * jg], bw[mt][2 * jg], zero);
-                    a = mfma_bf16(xs[2 * jg + 1], bw[mt][2 * jg + 1], a);
-#pragma unroll
-                    for (int i = 0; i < MTC; ++i)
-                        acc[mt][tb][i] = fmaf(sg[mt][jg], fmaf(-zg[mt][jg], o[i], a[i]), acc[mt][tb][i]);
-                }
-            }
+            for (int d = 0; d < 4; ++d) W.bw[mt][d] = unpack_int4_biased(cq[mt][d]);
+            W.sg[mt][0] = bf16lo_f32(cs[mt]);
+            W.sg[mt][1] = bf16hi_f32(cs[mt]);
+            W.zg[mt][0] = bf16lo_f32(cz[mt]) + 128.0f;
+            W.zg[mt][1] = bf16hi_f32(cz[mt]) + 128.0f;
         }
     } else {
-        u32x4 bw[NMAT][2];
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
                 const u32x2 p0 = unpack_int8_biased(cq[mt][2 * d]);
                 const u32x2 p1 = unpack_int8_biased(cq[mt][2 * d + 1]);
-                bw[mt][d] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+                W.bw[mt][d] = u32x4{p0[0], p0[1], p1[0], p1[1]};
             }
+    }
+}
+
+template <int FMT, int NMAT, int NT, int MT, typename XLoad>
+__device__ __forceinline__ void contract(const Widened<FMT, NMAT>& W, XLoad&& xl, float (&acc)[NMAT][NT][4],
+                                         f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT])
+{
+    constexpr int MTC = (NT == 1) ? MT : 4;
+    constexpr int STEPS = FmtT<FMT>::STEPS;
+    const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tb = 0; tb < NT; ++tb) {
-            u32x4 xs[STEPS];
-            xl(tb, xs);
+    for (int tb = 0; tb < NT; ++tb) {
+        u32x4 xs[STEPS];
+        xl(tb, xs);
+        if constexpr (FMT == FMT_INT4) {
+#pragma unroll
+            for (int jg = 0; jg < 2; ++jg) {
+                f32x4 o = mfma_bf16(xs[2 * jg], ones, zero);
+                o = mfma_bf16(xs[2 * jg + 1], ones, o);
+#pragma unroll
+                for (int mt = 0; mt < NMAT; ++mt) {
+                    f32x4 a = mfma_bf16(xs[2 * jg], W.bw[mt][2 * jg], zero);
+                    a = mfma_bf16(xs[2 * jg + 1], W.bw[mt][2 * jg + 1], a);
+#pragma unroll
+                    for (int i = 0; i < MTC; ++i)
+                        acc[mt][tb][i] = fmaf(W.sg[mt][jg], fmaf(-W.zg[mt][jg], o[i], a[i]), acc[mt][tb][i]);
+                }
+            }
+        } else {
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
                 one[tb] = mfma_bf16(xs[d], ones, one[tb]);
 #pragma unroll
-                for (int mt = 0; mt < NMAT; ++mt) tot[mt][tb] = mfma_bf16(xs[d], bw[mt][d], tot[mt][tb]);
+                for (int mt = 0; mt < NMAT; ++mt) tot[mt][tb] = mfma_bf16(xs[d], W.bw[mt][d], tot[mt][tb]);
             }
         }
     }
@@ -288,8 +356,9 @@ __device__ __forceinline__ void compute_step(const u32x4 (&cq)[NMAT], const uint
 // --------------------------------------------------------------------------
 // The tiled stream of one wave: `ntiles` tiles, steps [s0, s1) of each, NMAT
 // matrices.  base(i, mt) is the (uniform) address of tile i of matrix mt.
-// stage() issues the activation staging (no waits); the ring is primed after
-// it and one vmcnt wait plus a barrier retires the staging.  end(i, tot, one)
+// stage.begin() issues the activation staging, the ring is primed, then
+// stage.finish() stores the last staged batch and a barrier publishes it.
+// end(i, tot, one)
 // runs after the last step of tile i (every wave of the workgroup calls it
 // the same number of times, also a wave whose step range is empty).
 template <int FMT, int NMAT, int NT, int MT, int PF, typename Base, typename Stage, typename End>
@@ -359,16 +428,11 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
             szs = r == 0;
             b = 8 * j + r - 1;
         }
-        if (szs) {
+        if (szs) {   // scale/zero step: to the wave's LDS
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt) *(u32x4*)(wsz + mt * kStep + lane * 16) = rq[slot][mt];
         } else {
             const int lb = b - kb0;
-            auto xl = [&](int tb, u32x4 (&xs)[STEPS]) {
-                const uint8_t* xb = L.x + xrow[tb] + (uint32_t)lb * (BK * 2) + xoff_b[tb];
-#pragma unroll
-                for (int d = 0; d < STEPS; ++d) xs[d] = *(const u32x4*)(xb + 64u * ((uint32_t)d ^ xoff_a[tb]));
-            };
             uint32_t cs_[NMAT], cz_[NMAT];
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt) {
@@ -381,7 +445,14 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
                     cz_[mt] = 0u;
                 }
             }
-            compute_step<FMT, NMAT, NT, MT>(rq[slot], cs_, cz_, xl, acc, tot, one);
+            Widened<FMT, NMAT> W;
+            widen<FMT, NMAT>(rq[slot], cs_, cz_, W);
+            auto xl = [&](int tb, u32x4 (&xs)[STEPS]) {
+                const uint8_t* xb = L.x + xrow[tb] + (uint32_t)lb * (BK * 2) + xoff_b[tb];
+#pragma unroll
+                for (int d = 0; d < STEPS; ++d) xs[d] = *(const u32x4*)(xb + 64u * ((uint32_t)d ^ xoff_a[tb]));
+            };
+            contract<FMT, NMAT, NT, MT>(W, xl, acc, tot, one);
         }
         if (++cs == len) {
             if constexpr (FMT == FMT_INT4) {
@@ -398,7 +469,7 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
         }
     };
 
-    stage();
+    stage.begin();
     __builtin_amdgcn_sched_barrier(0);
     if (total > 0) {
         set_base(0);
@@ -406,13 +477,8 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
         for (int s = 0; s < PF; ++s) issue(s);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (total > 0)
-        wait_vmcnt<PF * NMAT>();
-    else
-        wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");   // no LDS read moves above the barrier
-    __builtin_amdgcn_sched_barrier(0);
+    stage.finish();
+    __syncthreads();
 
     if (len <= 0) {
         for (int i = 0; i < ntiles; ++i) end(i, tot, one);
@@ -498,9 +564,6 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
 
     const int n_units = (J.routed ? J.pv.n_union() : 1) * T;
     const int G = gridDim.x;
-    MatDev mats[NMAT];
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) mats[mt] = MatDev{};
     for (int u0 = blockIdx.x; u0 < n_units;) {
         const int item = u0 / T;
         int run = 0;
@@ -517,9 +580,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                 const int Rc = min(J.rows_cap, RR - c0);
                 if (tid < Rc) rows(it, c0, tid, roff, orows);
                 __syncthreads();
-                auto stage = [&]() {
-                    stage_issue<FMT, false, NMAT>(L, J.src, Rc, kb0, kb1 - kb0, false, mats, 0, 0, 1, KS, w);
-                };
+                RegStager<FMT> stage(L, J.src, Rc, kb0);
                 auto end = [&](int i, f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT]) {
                     const int tile = tile_of(i);
                     const int row0 = tile * 16;
@@ -627,7 +688,7 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
         orows[t] = orow;
     };
     auto finish = [&](int orow, int n, const float (&v)[2]) {
-        const float a = (float)(act_f64(p.act, (double)v[0]) * (double)v[1]);
+        const float a = act_f32(p.act, v[0]) * v[1];
         uint16_t hi, lo;
         split_bf16(a, hi, lo);
         const size_t o = (size_t)(2 * orow) * p.N + cons_index(p.dfmt, n);
