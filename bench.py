@@ -41,9 +41,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("moe_expert_dequant_amd/csrc/qgemm.h", "moe_expert_dequant_amd/csrc/device.h",
-                  "moe_expert_dequant_amd/csrc/ffnq.hip")
-TRAFFIC_FILE = "profiles/traffic_gu_kernel_int4_llama3-8b_m1.txt"
+KERNEL_SOURCES = tuple(f"moe_expert_dequant_amd/csrc/{f}" for f in
+                       ("device.h", "qgemm.h", "tiled.h", "route.h", "tail.h", "ffnq.hip"))
+TRAFFIC_FILE = "profiles/traffic_gu_tiled_kernel_int4_llama3-8b_m1.txt"
 
 
 def weight_bytes(fmt: int, n: int, k: int) -> int:
