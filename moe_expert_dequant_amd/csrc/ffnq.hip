@@ -322,12 +322,15 @@ KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_t
 #define FFNQ_GUT_CASE(F, NT_, MT_)                                                                         \
     if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                          \
         hipExtLaunchKernelGGL((gu_tiled_kernel<F, NT_, MT_>), dim3(c.grid), dim3(64 * c.ks), c.lds, stream, \
-                              phase_event(0), phase_event(1), 0, prm);                                     \
+                              phase_event(0), phase_event(1), 0, q);                                       \
         return true;                                                                                       \
     }
 
 bool launch_gu_tiled(int fmt, const KConfig& c, hipStream_t stream, const GUParams& prm)
 {
+    GUParams q = prm;   // the kernels take the launch shape as arguments (cheaper than reading it back)
+    q.ks = c.ks;
+    q.grid = c.grid;
     FFNQ_GUT_CASE(FMT_INT4, 1, 1) FFNQ_GUT_CASE(FMT_INT4, 1, 2) FFNQ_GUT_CASE(FMT_INT4, 1, 4)
     FFNQ_GUT_CASE(FMT_INT4, 2, 4) FFNQ_GUT_CASE(FMT_INT8, 1, 1) FFNQ_GUT_CASE(FMT_INT8, 1, 2)
     FFNQ_GUT_CASE(FMT_INT8, 1, 4) FFNQ_GUT_CASE(FMT_INT8, 2, 4)
@@ -337,12 +340,15 @@ bool launch_gu_tiled(int fmt, const KConfig& c, hipStream_t stream, const GUPara
 #define FFNQ_DNT_CASE(F, NT_, MT_)                                                                           \
     if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                            \
         hipExtLaunchKernelGGL((down_tiled_kernel<F, NT_, MT_>), dim3(c.grid, c.kg), dim3(64 * c.ks), c.lds,   \
-                              stream, phase_event(2), phase_event(3), 0, prm);                               \
+                              stream, phase_event(2), phase_event(3), 0, q);                                 \
         return true;                                                                                         \
     }
 
 bool launch_down_tiled(int fmt, const KConfig& c, hipStream_t stream, const DownParams& prm)
 {
+    DownParams q = prm;
+    q.ks = c.ks;
+    q.grid = c.grid;
     FFNQ_DNT_CASE(FMT_INT4, 1, 2) FFNQ_DNT_CASE(FMT_INT4, 1, 4) FFNQ_DNT_CASE(FMT_INT4, 2, 4)
     FFNQ_DNT_CASE(FMT_INT4, 4, 4) FFNQ_DNT_CASE(FMT_INT8, 1, 2) FFNQ_DNT_CASE(FMT_INT8, 1, 4)
     FFNQ_DNT_CASE(FMT_INT8, 2, 4) FFNQ_DNT_CASE(FMT_INT8, 4, 4)

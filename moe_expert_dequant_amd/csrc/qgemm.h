@@ -486,6 +486,7 @@ struct GUParams {
     const uint8_t* tgate;      // tiled formats: packed gate / up (expert 0)
     const uint8_t* tup;
     long long tebytes;         // tiled bytes per expert
+    int ks, grid;              // tiled kernels: waves per workgroup and gridDim.x, as launched
 };
 
 template <int FMT, int NT, int MT>
@@ -629,6 +630,7 @@ struct DownParams {
     const float* logit;        // [m] (SIGMOID)
     const uint8_t* tdown;      // tiled formats: packed down (expert 0)
     long long tebytes;         // tiled bytes per expert
+    int ks, grid;              // tiled kernels: waves per workgroup and gridDim.x, as launched
 };
 
 __device__ __forceinline__ void down_finish(const DownParams& p, int t, int n, float h)

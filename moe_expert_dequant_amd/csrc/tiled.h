@@ -28,13 +28,10 @@
 //   Rows >= N of the last tile are zero codes with zero scales.
 //   Experts of a stack follow each other, expert_bytes apart.
 //
-// Kernels:
-//   gu_tiled_kernel   -- every wave owns whole tiles (gate and up over all of
-//                        K): no cross-wave reduction; the waves of a
-//                        workgroup share the activation rows staged in LDS;
-//                        scale/zero steps land in wave-private LDS.
-//   down_tiled_kernel -- the waves of a workgroup split a tile's K range by
-//                        scale/zero groups; one LDS reduction per tile.
+// Kernels (gu_tiled_kernel: gate and up; down_tiled_kernel: down and tail):
+// the waves of a workgroup split a tile's K range by scale/zero groups (INT4)
+// or blocks (INT8) and meet in one LDS reduction per tile; they share the
+// activation rows staged in LDS; scale/zero steps land in wave-private LDS.
 // The register ring of code steps runs across tile boundaries.
 #pragma once
 #include "qgemm.h"
@@ -224,18 +221,23 @@ __device__ __forceinline__ float tile_row_scale(const uint8_t* p, int lr)
 // batches of kSR per thread; every batch issues all of its loads before its
 // stores, and the last batch's stores are deferred to finish(), so that the
 // caller can issue the weight ring in between and one wait covers both.
+// Row r's source offset is direct0 + r*rstride when direct0 >= 0 (rows that
+// follow each other in the source: no row table needed, so staging can start
+// before the table is written), else the row table L.roff[r].
 constexpr int kSR = 8;
 
 template <int FMT>
 struct RegStager {
     const Lds& L;
     const uint16_t* src;
-    int Rc, kb0, xslots;
+    int Rc, kb0, xslots, nthr;
+    long long direct0, rstride;
     u32x4 v[kSR];
     int slot[kSR];
 
-    __device__ __forceinline__ RegStager(const Lds& l, const uint16_t* s, int rc, int k0)
-        : L(l), src(s), Rc(rc), kb0(k0), xslots(rc * l.per_row) {}
+    __device__ __forceinline__ RegStager(const Lds& l, const uint16_t* s, int rc, int k0, int nt, long long d0,
+                                         long long rs)
+        : L(l), src(s), Rc(rc), kb0(k0), xslots(rc * l.per_row), nthr(nt), direct0(d0), rstride(rs) {}
 
     __device__ __forceinline__ void load(int base)
     {
@@ -243,10 +245,11 @@ struct RegStager {
         const int per_row = L.per_row;
 #pragma unroll
         for (int i = 0; i < kSR; ++i) {
-            const int sl = min(base + (int)threadIdx.x + i * (int)blockDim.x, xslots - 1);
+            const int sl = min(base + (int)threadIdx.x + i * nthr, xslots - 1);
             const int rr = sl / per_row, jp = sl - rr * per_row;
             const int lb = jp / CPB, ci = (jp - lb * CPB) ^ ((rr >> L.swz_shift) & L.swz_mask);
-            v[i] = *(const u32x4*)(src + L.roff[rr] + (kb0 + lb) * BK + ci * 8);
+            const long long ro = direct0 >= 0 ? direct0 + rr * rstride : L.roff[rr];
+            v[i] = *(const u32x4*)(src + ro + (kb0 + lb) * BK + ci * 8);
             slot[i] = sl;
         }
     }
@@ -258,7 +261,7 @@ struct RegStager {
     // all batches but the last, then the last batch's loads
     __device__ __forceinline__ void begin()
     {
-        const int step = kSR * (int)blockDim.x;
+        const int step = kSR * nthr;
         int base = 0;
         for (; base + step < xslots; base += step) {
             load(base);
@@ -354,20 +357,63 @@ __device__ __forceinline__ void contract(const Widened<FMT, NMAT>& W, XLoad&& xl
 }
 
 // --------------------------------------------------------------------------
-// The tiled stream of one wave: `ntiles` tiles, steps [s0, s1) of each, NMAT
-// matrices.  base(i, mt) is the (uniform) address of tile i of matrix mt.
-// stage.begin() issues the activation staging, the ring is primed, then
-// stage.finish() stores the last staged batch and a barrier publishes it.
-// end(i, tot, one)
-// runs after the last step of tile i (every wave of the workgroup calls it
-// the same number of times, also a wave whose step range is empty).
-template <int FMT, int NMAT, int NT, int MT, int PF, typename Base, typename Stage, typename End>
-__device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0, const Lds& L, int Rc, uint8_t* wsz,
-                                             Base base, Stage stage, End end)
+// The register ring of one wave: `ntiles` tiles, steps [s0, s1) of each, NMAT
+// matrices, PF steps in flight.  base(i, mt) is the (uniform) address of tile
+// i of matrix mt.  prime() issues the first PF steps; it runs before anything
+// else the workgroup does for these tiles (row tables, barrier, activation
+// staging), so that HBM is busy from the start of the kernel.
+template <int NMAT, int PF, typename Base>
+struct TRing {
+    Base base;
+    int ntiles, s0, len;
+    int it = 0, is = 0;       // issue cursor: tile, step (relative to s0)
+    const uint8_t* ib[NMAT];
+    u32x4 rq[PF][NMAT];
+
+    __device__ __forceinline__ TRing(Base b, int nt, int first, int last)
+        : base(b), ntiles(nt), s0(first), len(last - first) {}
+
+    __device__ __forceinline__ void set_base(int t)
+    {
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) ib[mt] = base(t, mt) + (size_t)s0 * kStep + (threadIdx.x & 63) * 16;
+    }
+    __device__ __forceinline__ void issue(int slot)
+    {
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+            rq[slot][mt] = __builtin_nontemporal_load((const u32x4*)(ib[mt] + (size_t)is * kStep));
+        if (is + 1 < len) {
+            ++is;
+        } else if (it + 1 < ntiles) {
+            ++it;
+            is = 0;
+            set_base(it);
+        }   // past the last step: the last step is loaded again (never consumed)
+    }
+    __device__ __forceinline__ void prime()
+    {
+        if (ntiles * len > 0) {
+            set_base(0);
+#pragma unroll
+            for (int s = 0; s < PF; ++s) issue(s);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+};
+
+// The tiled stream of one wave over the ring's tiles.  The ring is primed and
+// stage.begin() has issued the activation staging; stage.finish() stores the
+// last staged batch and a barrier publishes it.  end(i, tot, one) runs after the
+// last step of tile i (every wave of the workgroup calls it the same number
+// of times, also a wave whose step range is empty).
+template <int FMT, int NMAT, int NT, int MT, int PF, typename Ring, typename Stage, typename End>
+__device__ __forceinline__ void tiled_stream(Ring& ring, int kb0, const Lds& L, int Rc, uint8_t* wsz, Stage stage,
+                                             End end)
 {
     constexpr int BK = FmtT<FMT>::BK, STEPS = FmtT<FMT>::STEPS;
     const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
-    const int len = s1 - s0;
+    const int ntiles = ring.ntiles, s0 = ring.s0, len = ring.len;
     const int total = ntiles * len;
 
     uint32_t xrow[NT], xoff_b[NT], xoff_a[NT];
@@ -396,27 +442,6 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
     };
     zero_acc();
 
-    // issue cursor: tile it, step is (relative to s0)
-    int it = 0, is = 0;
-    const uint8_t* ib[NMAT];
-    auto set_base = [&](int t) {
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) ib[mt] = base(t, mt) + (size_t)s0 * kStep + lane * 16;
-    };
-    u32x4 rq[PF][NMAT];
-    auto issue = [&](int slot) {
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
-            rq[slot][mt] = __builtin_nontemporal_load((const u32x4*)(ib[mt] + (size_t)is * kStep));
-        if (is + 1 < len) {
-            ++is;
-        } else if (it + 1 < ntiles) {
-            ++it;
-            is = 0;
-            set_base(it);
-        }   // past the last step: the last step is loaded again (never consumed)
-    };
-
     // consume cursor
     int ct = 0, cs = 0;
     auto consume = [&](int slot) {
@@ -430,7 +455,7 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
         }
         if (szs) {   // scale/zero step: to the wave's LDS
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) *(u32x4*)(wsz + mt * kStep + lane * 16) = rq[slot][mt];
+            for (int mt = 0; mt < NMAT; ++mt) *(u32x4*)(wsz + mt * kStep + lane * 16) = ring.rq[slot][mt];
         } else {
             const int lb = b - kb0;
             uint32_t cs_[NMAT], cz_[NMAT];
@@ -446,7 +471,7 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
                 }
             }
             Widened<FMT, NMAT> W;
-            widen<FMT, NMAT>(rq[slot], cs_, cz_, W);
+            widen<FMT, NMAT>(ring.rq[slot], cs_, cz_, W);
             auto xl = [&](int tb, u32x4 (&xs)[STEPS]) {
                 const uint8_t* xb = L.x + xrow[tb] + (uint32_t)lb * (BK * 2) + xoff_b[tb];
 #pragma unroll
@@ -469,14 +494,6 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
         }
     };
 
-    stage.begin();
-    __builtin_amdgcn_sched_barrier(0);
-    if (total > 0) {
-        set_base(0);
-#pragma unroll
-        for (int s = 0; s < PF; ++s) issue(s);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     stage.finish();
     __syncthreads();
 
@@ -490,7 +507,7 @@ __device__ __forceinline__ void tiled_stream(int ntiles, int s0, int s1, int kb0
         for (int s = 0; s < PF; ++s) {
             consume(s);
             __builtin_amdgcn_sched_barrier(0);
-            issue(s);
+            ring.issue(s);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -528,6 +545,7 @@ struct TiledJob {
     int m, act_rows;
     const int32_t* topk_ids;
     int n_experts;
+    int KS, G;                // waves per workgroup, gridDim.x
 };
 
 template <int FMT, int NMAT, int NT, int MT, bool HILO, typename Rows, typename Finish>
@@ -535,54 +553,58 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int PER = HILO ? NT * 2 : NMAT * NT * 4;   // reduction floats per lane and wave
-    const int KS = uniform(blockDim.x >> 6);
+    const int KS = J.KS;
     const int w = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int tid = threadIdx.x, nthr = 64 * KS;
     const TileGeo geo = tile_geo(FMT, J.N, J.K);
     const int T = geo.T;
     const int nun = FMT == FMT_INT4 ? geo.ng : geo.nbk;   // K units: groups or blocks
-    const int U0 = (int)(((long long)nun * blockIdx.y) / J.KG), U1 = (int)(((long long)nun * (blockIdx.y + 1)) / J.KG);
+    // K range of this grid row and of this wave (32-bit: nun * KG is small)
+    const int U0 = nun * (int)blockIdx.y / J.KG, U1 = nun * ((int)blockIdx.y + 1) / J.KG;
     const int kb0 = FMT == FMT_INT4 ? 8 * U0 : U0;
     const int kb1 = FMT == FMT_INT4 ? min(8 * U1, geo.nbk) : U1;
     const int u0w = U0 + (U1 - U0) * w / KS, u1w = U0 + (U1 - U0) * (w + 1) / KS;
     const int s0 = FMT == FMT_INT4 ? 9 * u0w : u0w;
     const int s1 = FMT == FMT_INT4 ? min(9 * u1w, geo.steps) : u1w;
-    const TLdsLayout LL = tiled_launch_lds(NMAT, FMT, J.N, J.K, J.KG, J.rows_cap, KS, PER);
-    Lds L;
-    L.x = smem;
-    L.per_row = (kb1 - kb0) * (FmtT<FMT>::BK / 8);
-    set_swizzle<FMT>(L);
-    L.sz = nullptr;
-    L.zstride = 1;
-    long long* roff = (long long*)(smem + LL.rows);
-    L.roff = roff;
-    int* orows = (int*)(smem + LL.orow);
-    uint8_t* wsz = smem + LL.wsz + (size_t)w * NMAT * kStep;
-    float* red = (float*)(smem + LL.red);
-    const size_t red_half = (size_t)KS * PER * 64;
 
     const int n_units = (J.routed ? J.pv.n_union() : 1) * T;
-    const int G = gridDim.x;
+    const int G = J.G;
     for (int u0 = blockIdx.x; u0 < n_units;) {
-        const int item = u0 / T;
-        int run = 0;
-        while (u0 + run * G < n_units && (u0 + run * G) / T == item) ++run;
+        int item = 0, run;
+        if (!J.routed) {
+            run = (n_units - u0 + G - 1) / G;   // every unit belongs to the one item
+        } else {
+            item = u0 / T;
+            run = 0;
+            while (u0 + run * G < n_units && (u0 + run * G) / T == item) ++run;
+        }
         const Item it = resolve_item(J.pv, J.routed, item, J.m, J.act_rows, J.topk_ids, J.n_experts);
         if (it.ok) {
             const uint8_t* eq[NMAT];
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt) eq[mt] = J.tq[mt] + (size_t)it.e * J.tebytes;
-            auto tile_of = [&](int i) { return (u0 + i * G) % T; };
-            auto base = [&](int i, int mt) { return eq[mt] + (size_t)tile_of(i) * geo.tile_bytes; };
+            const int t0 = u0 - item * T;   // tile of the run's first unit; later ones are G tiles apart
+            auto base = [&](int i, int mt) { return eq[mt] + (size_t)(t0 + i * G) * geo.tile_bytes; };
             const int RR = J.rows_per_item_mul * it.R;
             for (int c0 = 0; c0 < RR; c0 += J.rows_cap) {
+                TRing<NMAT, kPfT, decltype(base)> ring(base, run, s0, s1);
+                const TLdsLayout LL = tiled_launch_lds(NMAT, FMT, J.N, J.K, J.KG, J.rows_cap, KS, PER);
+                Lds L;
+                L.x = smem;
+                L.per_row = (kb1 - kb0) * (FmtT<FMT>::BK / 8);
+                set_swizzle<FMT>(L);
+                L.sz = nullptr;
+                L.zstride = 1;
+                long long* roff = (long long*)(smem + LL.rows);
+                L.roff = roff;
+                int* orows = (int*)(smem + LL.orow);
+                uint8_t* wsz = smem + LL.wsz + (size_t)w * NMAT * kStep;
+                float* red = (float*)(smem + LL.red);
+                const size_t red_half = (size_t)KS * PER * 64;
                 const int Rc = min(J.rows_cap, RR - c0);
-                if (tid < Rc) rows(it, c0, tid, roff, orows);
-                __syncthreads();
-                RegStager<FMT> stage(L, J.src, Rc, kb0);
                 auto end = [&](int i, f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT]) {
-                    const int tile = tile_of(i);
+                    const int tile = t0 + i * G;
                     const int row0 = tile * 16;
                     float* rb = red + (size_t)(i & 1) * red_half;
 #pragma unroll
@@ -638,7 +660,24 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                         finish(orow, n, v);
                     }
                 };
-                tiled_stream<FMT, NMAT, NT, MT, kPfT>(run, s0, s1, kb0, L, Rc, wsz, base, stage, end);
+                if (!J.routed) {
+                    // dense: staged row r is source row c0 + r, so the activation loads go out
+                    // first (ahead of the weight burst), then the ring, then the row table
+                    RegStager<FMT> stage(L, J.src, Rc, kb0, nthr, (long long)c0 * J.K, J.K);
+                    stage.begin();
+                    __builtin_amdgcn_sched_barrier(0);
+                    ring.prime();
+                    if (tid < Rc) rows(it, c0, tid, roff, orows);
+                    tiled_stream<FMT, NMAT, NT, MT, kPfT>(ring, kb0, L, Rc, wsz, stage, end);
+                } else {
+                    ring.prime();
+                    if (tid < Rc) rows(it, c0, tid, roff, orows);
+                    __syncthreads();
+                    RegStager<FMT> stage(L, J.src, Rc, kb0, nthr, -1, 0);
+                    stage.begin();
+                    __builtin_amdgcn_sched_barrier(0);
+                    tiled_stream<FMT, NMAT, NT, MT, kPfT>(ring, kb0, L, Rc, wsz, stage, end);
+                }
                 __syncthreads();
             }
         }
@@ -646,22 +685,23 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
     }
 }
 
-// gate + up + activation: f(gate)*up per (token or pair, inter row), computed
-// in double, rounded to fp32 and written as the bf16 hi/lo pair in the down
-// matrix's consumption order (act row 2r = hi, 2r+1 = lo).
+// gate + up + activation: f(gate)*up per (token or pair, inter row) in fp32,
+// written as the bf16 hi/lo pair (act row 2r = hi, 2r+1 = lo) in the order the
+// down kernel reads (natural for tiled down weights).
+//
+// Both tiled kernels read the kernel arguments they use into SGPRs at entry:
+// an empty asm statement takes them all as inputs, so they are fetched up
+// front instead of in the block that first needs each (dependent round trips
+// that would delay the first weight loads of every wave).  Inputs only: the
+// values, and what the compiler knows of the pointers, are unchanged.  The
+// launch shape comes in the arguments too (ks, grid) rather than from the
+// dispatch packet.
 template <int FMT, int NT, int MT>
 __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
 {
-    if (p.gate_vec != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
-        const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-        for (int t = w; t < p.m; t += nw) {
-            double acc = 0.0;
-            for (int i = lane; i < p.K; i += 64)
-                acc += (double)bf16_f32(p.gate_vec[i]) * (double)bf16_f32(p.x[(size_t)t * p.K + i]);
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (lane == 0) p.logit[t] = (float)acc;
-        }
-    }
+    asm volatile("" ::"s"(p.tgate), "s"(p.tup), "s"(p.tebytes), "s"(p.N), "s"(p.K), "s"(p.x), "s"(p.rows_cap),
+                 "s"(p.plan), "s"(p.m), "s"(p.top_k), "s"(p.act_rows), "s"(p.topk_ids), "s"(p.n_experts), "s"(p.act),
+                 "s"(p.dfmt), "s"(p.act_out), "s"(p.gate_vec), "s"(p.logit), "s"(p.ks), "s"(p.grid));
     TiledJob J;
     J.tq[0] = p.tgate;
     J.tq[1] = p.tup;
@@ -672,30 +712,50 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
     J.src = p.x;
     J.rows_cap = p.rows_cap;
     J.rows_per_item_mul = 1;
-    J.routed = p.plan != nullptr;
-    J.pv = PlanView{p.plan, p.m, p.top_k};
+    const int32_t* plan = p.plan;
+    J.routed = plan != nullptr;
     J.m = p.m;
+    const int top_k = p.top_k;
+    J.pv = PlanView{plan, J.m, top_k};
     J.act_rows = p.act_rows;
     J.topk_ids = p.topk_ids;
     J.n_experts = p.n_experts;
+    J.KS = p.ks;
+    J.G = p.grid;
+    const int act = p.act, dfmt = p.dfmt;
+    uint16_t* const act_out = p.act_out;
+    const uint16_t* const gate_vec = p.gate_vec;
+    float* const logit = p.logit;
     auto rows = [&](const Item& it, int c0, int t, long long* roff, int* orows) {
         int tok = c0 + t, orow = c0 + t;
         if (J.routed) {
-            orow = item_pair(J.pv, it, c0 + t, p.act_rows);
-            tok = orow < 0 ? 0 : orow / p.top_k;
+            orow = item_pair(J.pv, it, c0 + t, J.act_rows);
+            tok = orow < 0 ? 0 : orow / top_k;
         }
-        roff[t] = (long long)tok * p.K;
+        roff[t] = (long long)tok * J.K;
         orows[t] = orow;
     };
     auto finish = [&](int orow, int n, const float (&v)[2]) {
-        const float a = act_f32(p.act, v[0]) * v[1];
+        const float a = act_f32(act, v[0]) * v[1];
         uint16_t hi, lo;
         split_bf16(a, hi, lo);
-        const size_t o = (size_t)(2 * orow) * p.N + cons_index(p.dfmt, n);
-        p.act_out[o] = hi;
-        p.act_out[o + p.N] = lo;
+        const size_t o = (size_t)(2 * orow) * J.N + cons_index(dfmt, n);
+        act_out[o] = hi;
+        act_out[o + J.N] = lo;
     };
     tiled_body<FMT, 2, NT, MT, false>(J, rows, finish);
+    // shared-expert gate logits (read by the down kernel's tail): one
+    // workgroup, after its tiles
+    if (gate_vec != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+        const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, nw = J.KS;
+        for (int t = w; t < J.m; t += nw) {
+            double acc = 0.0;
+            for (int i = lane; i < J.K; i += 64)
+                acc += (double)bf16_f32(gate_vec[i]) * (double)bf16_f32(J.src[(size_t)t * J.K + i]);
+            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+            if (lane == 0) logit[t] = (float)acc;
+        }
+    }
 }
 
 // down + tail: h per (token or pair, hidden row), finished by down_finish
@@ -703,6 +763,9 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
 template <int FMT, int NT, int MT>
 __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
 {
+    asm volatile("" ::"s"(p.tdown), "s"(p.tebytes), "s"(p.N), "s"(p.K), "s"(p.KG), "s"(p.act), "s"(p.rows_cap),
+                 "s"(p.plan), "s"(p.m), "s"(p.top_k), "s"(p.act_rows), "s"(p.topk_ids), "s"(p.n_experts), "s"(p.tail),
+                 "s"(p.out), "s"(p.part), "s"(p.logit), "s"(p.ks), "s"(p.grid));
     TiledJob J;
     J.tq[0] = p.tdown;
     J.tq[1] = nullptr;
@@ -713,17 +776,20 @@ __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
     J.src = p.act;
     J.rows_cap = p.rows_cap;
     J.rows_per_item_mul = 2;
-    J.routed = p.plan != nullptr;
-    J.pv = PlanView{p.plan, p.m, p.top_k};
+    const int32_t* plan = p.plan;
+    J.routed = plan != nullptr;
     J.m = p.m;
+    J.pv = PlanView{plan, J.m, p.top_k};
     J.act_rows = p.act_rows;
     J.topk_ids = p.topk_ids;
     J.n_experts = p.n_experts;
+    J.KS = p.ks;
+    J.G = p.grid;
     auto rows = [&](const Item& it, int c0, int t, long long* roff, int* orows) {
         const int xr = c0 + t, li = xr >> 1;
         int arow = li;
-        if (J.routed) arow = item_pair(J.pv, it, li, p.act_rows);
-        roff[t] = (long long)(2 * (arow < 0 ? 0 : arow) + (xr & 1)) * p.K;
+        if (J.routed) arow = item_pair(J.pv, it, li, J.act_rows);
+        roff[t] = (long long)(2 * (arow < 0 ? 0 : arow) + (xr & 1)) * J.K;
         if ((t & 1) == 0) orows[t >> 1] = arow;
     };
     auto finish = [&](int orow, int n, const float (&v)[1]) { down_finish(p, orow, n, v[0]); };
