@@ -264,7 +264,7 @@ KConfig gu_tiled_config(int fmt, int K, int N, long long items_est, int rows_tot
     c.ks = is_int4(fmt) ? tiled_ks(nun, items_est * geo.T, cus, 8, 8)
                         : tiled_ks(std::max(1, nun / max_units_per_wave_int8), items_est * geo.T, cus, 8, 8);
     for (;;) {
-        c.lds = tiled_launch_lds(2, F, N, K, 1, c.rows_cap, c.ks, 2 * c.nt * 4).total;
+        c.lds = tiled_launch_lds(2, F, N, K, 1, c.rows_cap, c.ks, 2 * c.nt * 4 * red_lanes(c.nt, c.rows_cap)).total;
         if (c.lds <= kLdsBudget || c.rows_cap <= 1) break;
         --c.rows_cap;
     }
@@ -290,7 +290,7 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total)
     d.rows_cap = std::min(rp, 16 * d.nt);
     int kg = std::max(1, (kRefCUs + geo.T - 1) / geo.T);
     kg = std::min(kg, nun);
-    while (kg < nun && tiled_launch_lds(1, F, N, K, kg, d.rows_cap, 8, 2 * d.nt).total > kLdsBudget) ++kg;
+    while (kg < nun && tiled_launch_lds(1, F, N, K, kg, d.rows_cap, 8, 2 * d.nt * 64).total > kLdsBudget) ++kg;
     d.kg = kg;
     const int upw = (nun + kg - 1) / kg;   // K units of the longest range
     if (is_int4(fmt)) {
@@ -314,7 +314,7 @@ KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_t
     c.rows_cap = d.rows_cap;
     c.kg = d.kg;
     c.ks = d.ks;
-    c.lds = tiled_launch_lds(1, F, N, K, d.kg, c.rows_cap, c.ks, 2 * c.nt).total;
+    c.lds = tiled_launch_lds(1, F, N, K, d.kg, c.rows_cap, c.ks, 2 * c.nt * red_lanes(c.nt, c.rows_cap)).total;
     c.grid = (int)std::max<long long>(1, std::min<long long>(items_est * geo.T, (long long)cus * 16));
     return c;
 }

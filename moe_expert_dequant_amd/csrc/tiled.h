@@ -164,8 +164,13 @@ struct TLdsLayout {
     size_t wsz, rows, orow, red, total;
 };
 
+// Lanes of a wave whose accumulators hold staged rows: with one 16-row MFMA
+// block and at most 4 staged rows only lanes 0-15 (D rows 0-3) do, and the
+// cross-wave reduction keeps just those.
+__host__ __device__ inline int red_lanes(int nt, int rows_cap) { return (nt == 1 && rows_cap <= 4) ? 16 : 64; }
+
 __host__ __device__ inline TLdsLayout tiled_lds(int nmat, int fmt, int nbk, int rows_cap, int nwaves,
-                                                int red_floats_per_lane)
+                                                int red_floats_per_wave)
 {
     TLdsLayout l;
     const int BK = fmt == FMT_INT4 ? 128 : 64;
@@ -175,7 +180,7 @@ __host__ __device__ inline TLdsLayout tiled_lds(int nmat, int fmt, int nbk, int 
     l.orow = l.rows + (size_t)rows_cap * 8;   // int32 output row of each staged row
     l.red = l.orow + (size_t)rows_cap * 4;
     l.red = (l.red + 15) & ~(size_t)15;
-    l.total = l.red + (size_t)2 * nwaves * red_floats_per_lane * 64 * 4;
+    l.total = l.red + (size_t)2 * nwaves * red_floats_per_wave * 4;
     return l;
 }
 
@@ -191,9 +196,9 @@ __host__ __device__ inline int tiled_nbk_max(int fmt, int n, int k, int KG)
 }
 
 __host__ __device__ inline TLdsLayout tiled_launch_lds(int nmat, int fmt, int n, int k, int KG, int rows_cap, int KS,
-                                                       int red_floats_per_lane)
+                                                       int red_floats_per_wave)
 {
-    return tiled_lds(nmat, fmt, tiled_nbk_max(fmt, n, k, KG), rows_cap, KS, red_floats_per_lane);
+    return tiled_lds(nmat, fmt, tiled_nbk_max(fmt, n, k, KG), rows_cap, KS, red_floats_per_wave);
 }
 
 // Sixteen fp32 row scales of an INT8 tile through the scalar cache (a
@@ -570,6 +575,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
 
     const int n_units = (J.routed ? J.pv.n_union() : 1) * T;
     const int G = J.G;
+    const int RL = red_lanes(NT, J.rows_cap);   // lanes kept by the reduction (uniform)
     for (int u0 = blockIdx.x; u0 < n_units;) {
         int item = 0, run;
         if (!J.routed) {
@@ -589,7 +595,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
             const int RR = J.rows_per_item_mul * it.R;
             for (int c0 = 0; c0 < RR; c0 += J.rows_cap) {
                 TRing<NMAT, kPfT, decltype(base)> ring(base, run, s0, s1);
-                const TLdsLayout LL = tiled_launch_lds(NMAT, FMT, J.N, J.K, J.KG, J.rows_cap, KS, PER);
+                const TLdsLayout LL = tiled_launch_lds(NMAT, FMT, J.N, J.K, J.KG, J.rows_cap, KS, PER * RL);
                 Lds L;
                 L.x = smem;
                 L.per_row = (kb1 - kb0) * (FmtT<FMT>::BK / 8);
@@ -601,7 +607,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                 int* orows = (int*)(smem + LL.orow);
                 uint8_t* wsz = smem + LL.wsz + (size_t)w * NMAT * kStep;
                 float* red = (float*)(smem + LL.red);
-                const size_t red_half = (size_t)KS * PER * 64;
+                const size_t red_half = (size_t)KS * PER * RL;
                 const int Rc = min(J.rows_cap, RR - c0);
                 auto end = [&](int i, f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT]) {
                     const int tile = t0 + i * G;
@@ -617,7 +623,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                                     vh = fmaf(-128.0f, one[tb][2 * h2], vh);
                                     vl = fmaf(-128.0f, one[tb][2 * h2 + 1], vl);
                                 }
-                                rb[((w * PER) + tb * 2 + h2) * 64 + lane] = vh + vl;
+                                if (lane < RL) rb[((w * PER) + tb * 2 + h2) * RL + lane] = vh + vl;
                             }
                         } else {
 #pragma unroll
@@ -626,7 +632,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                                 for (int i2 = 0; i2 < 4; ++i2) {
                                     float v = tot[mt][tb][i2];
                                     if constexpr (FMT == FMT_INT8) v = fmaf(-128.0f, one[tb][i2], v);
-                                    rb[((w * PER) + (mt * NT + tb) * 4 + i2) * 64 + lane] = v;
+                                    if (lane < RL) rb[((w * PER) + (mt * NT + tb) * 4 + i2) * RL + lane] = v;
                                 }
                         }
                     }
@@ -653,7 +659,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                             for (int ww = 0; ww < KS; ++ww) {
                                 const int slot = HILO ? (ww * PER + tb * 2 + ((rl & 3) >> 1))
                                                       : (ww * PER + (mt * NT + tb) * 4 + (rl & 3));
-                                h += rb[slot * 64 + ln];
+                                h += rb[slot * RL + ln];
                             }
                             v[mt] = FMT == FMT_INT8 ? sc[mt] * h : h;
                         }
