@@ -138,6 +138,7 @@ struct KConfig {
     int nt, mt, ks, rows_cap, kg;
     size_t lds;
     int grid;   // tiled kernels: workgroups along x
+    int ts;     // tiled kernels: waves take turns over tiles (1) or split K (0)
 };
 
 KConfig gu_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
@@ -264,7 +265,7 @@ KConfig gu_tiled_config(int fmt, int K, int N, long long items_est, int rows_tot
     c.ks = is_int4(fmt) ? tiled_ks(nun, items_est * geo.T, cus, 8, 8)
                         : tiled_ks(std::max(1, nun / max_units_per_wave_int8), items_est * geo.T, cus, 8, 8);
     for (;;) {
-        c.lds = tiled_launch_lds(2, F, N, K, 1, c.rows_cap, c.ks, 2 * c.nt * 4 * red_lanes(c.nt, c.rows_cap)).total;
+        c.lds = tiled_launch_lds(2, F, N, K, 1, c.rows_cap, c.ks, c.ts ? 0 : 2 * c.nt * 4 * red_lanes(c.nt, c.rows_cap)).total;
         if (c.lds <= kLdsBudget || c.rows_cap <= 1) break;
         --c.rows_cap;
     }
@@ -272,13 +273,19 @@ KConfig gu_tiled_config(int fmt, int K, int N, long long items_est, int rows_tot
     return c;
 }
 
-// K split of the tiled down projection (device independent, so that the
-// workspace size is too): K ranges across workgroups (kg) and waves (ks).
+// Split of the tiled down projection (device independent, so that the
+// workspace size is too): K ranges across workgroups (kg), and either K
+// ranges across the ks waves (K split) or tiles across them (ts, tile split).
+// Dense calls with two or more tokens take the tile split: staging 2 rows per
+// token over a whole K range for a single tile would move more bytes from L2
+// than the tile's weights; with four tiles per workgroup and K cut into
+// about 7 ranges the staged rows serve four tiles and the grid still fills
+// the chip.  The fp32 partials of the K ranges are summed by the tail kernel.
 struct DSplit {
-    int kg, ks, rows_cap, nt;
+    int kg, ks, rows_cap, nt, ts, gx;
 };
 
-DSplit down_tiled_split(int fmt, int K, int N, int rows_total)
+DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense)
 {
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
@@ -291,7 +298,7 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total)
     int kg = std::max(1, (kRefCUs + geo.T - 1) / geo.T);
     kg = std::min(kg, nun);
     while (kg < nun && tiled_launch_lds(1, F, N, K, kg, d.rows_cap, 8, 2 * d.nt * 64).total > kLdsBudget) ++kg;
-    d.kg = kg;
+    d.kg = std::min(kg, nun);   // every K range holds at least one K unit (the kernels rely on it)
     const int upw = (nun + kg - 1) / kg;   // K units of the longest range
     if (is_int4(fmt)) {
         // fewest waves that give every wave the minimal number of groups
@@ -300,12 +307,22 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total)
     } else {
         d.ks = std::max(1, std::min(8, upw / 4));
     }
+    if (dense && rows_total >= 2) {
+        d.ts = 1;
+        d.ks = 4;
+        d.gx = (geo.T + d.ks - 1) / d.ks;
+        const long long per_range = (long long)d.ks * d.gx;   // waves of one K range
+        int tk = (int)((7LL * kRefCUs + per_range / 2) / per_range);   // ~7 waves per CU in all
+        tk = std::max(1, std::min(tk, nun));
+        while (tk < nun && tiled_launch_lds(1, F, N, K, tk, d.rows_cap, d.ks, 0).total > kLdsBudget) ++tk;
+        d.kg = tk;
+    }
     return d;
 }
 
-KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus, bool dense)
 {
-    const DSplit d = down_tiled_split(fmt, K, N, rows_total);
+    const DSplit d = down_tiled_split(fmt, K, N, rows_total, dense);
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
     KConfig c{};
@@ -314,16 +331,21 @@ KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_t
     c.rows_cap = d.rows_cap;
     c.kg = d.kg;
     c.ks = d.ks;
-    c.lds = tiled_launch_lds(1, F, N, K, d.kg, c.rows_cap, c.ks, 2 * c.nt * red_lanes(c.nt, c.rows_cap)).total;
-    c.grid = (int)std::max<long long>(1, std::min<long long>(items_est * geo.T, (long long)cus * 16));
+    c.ts = d.ts;
+    c.lds = tiled_launch_lds(1, F, N, K, d.kg, c.rows_cap, c.ks, c.ts ? 0 : 2 * c.nt * red_lanes(c.nt, c.rows_cap)).total;
+    c.grid = c.ts ? d.gx : (int)std::max<long long>(1, std::min<long long>(items_est * geo.T, (long long)cus * 16));
     return c;
 }
 
-#define FFNQ_GUT_CASE(F, NT_, MT_)                                                                         \
-    if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                          \
-        hipExtLaunchKernelGGL((gu_tiled_kernel<F, NT_, MT_>), dim3(c.grid), dim3(64 * c.ks), c.lds, stream, \
-                              phase_event(0), phase_event(1), 0, q);                                       \
-        return true;                                                                                       \
+#define FFNQ_GUT_CASE(F, NT_, MT_)                                                                           \
+    if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                            \
+        if (c.ts)                                                                                            \
+            hipExtLaunchKernelGGL((gu_tiled_kernel<F, NT_, MT_, true>), dim3(c.grid), dim3(64 * c.ks), c.lds, \
+                                  stream, phase_event(0), phase_event(1), 0, q);                             \
+        else                                                                                                 \
+            hipExtLaunchKernelGGL((gu_tiled_kernel<F, NT_, MT_, false>), dim3(c.grid), dim3(64 * c.ks), c.lds, \
+                                  stream, phase_event(0), phase_event(1), 0, q);                             \
+        return true;                                                                                         \
     }
 
 bool launch_gu_tiled(int fmt, const KConfig& c, hipStream_t stream, const GUParams& prm)
@@ -339,8 +361,12 @@ bool launch_gu_tiled(int fmt, const KConfig& c, hipStream_t stream, const GUPara
 
 #define FFNQ_DNT_CASE(F, NT_, MT_)                                                                           \
     if (fmt == F && c.nt == NT_ && c.mt == MT_) {                                                            \
-        hipExtLaunchKernelGGL((down_tiled_kernel<F, NT_, MT_>), dim3(c.grid, c.kg), dim3(64 * c.ks), c.lds,   \
-                              stream, phase_event(2), phase_event(3), 0, q);                                 \
+        if (c.ts)                                                                                            \
+            hipExtLaunchKernelGGL((down_tiled_kernel<F, NT_, MT_, true>), dim3(c.grid, c.kg), dim3(64 * c.ks), \
+                                  c.lds, stream, phase_event(2), phase_event(3), 0, q);                      \
+        else                                                                                                 \
+            hipExtLaunchKernelGGL((down_tiled_kernel<F, NT_, MT_, false>), dim3(c.grid, c.kg), dim3(64 * c.ks), \
+                                  c.lds, stream, phase_event(2), phase_event(3), 0, q);                      \
         return true;                                                                                         \
     }
 
@@ -356,9 +382,9 @@ bool launch_down_tiled(int fmt, const KConfig& c, hipStream_t stream, const Down
 }
 
 // K ranges of the down projection for a format (row-major or tiled).
-int down_ranges(int fmt, int K, int N, int rows_total)
+int down_ranges(int fmt, int K, int N, int rows_total, bool dense)
 {
-    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total).kg : down_kg(fmt, K, N, rows_total);
+    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total, dense).kg : down_kg(fmt, K, N, rows_total);
 }
 
 // ---------------------------------------------------------------------------
@@ -372,7 +398,7 @@ DenseWs dense_ws(int fmt_down, int hidden, int inter, int m)
 {
     DenseWs w{};
     size_t o = 0;
-    const int kg = down_ranges(fmt_down, inter, hidden, m);
+    const int kg = down_ranges(fmt_down, inter, hidden, m, true);
     w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * m * hidden * sizeof(float), 256);
     w.logit = o; o += align_up((size_t)m * sizeof(float), 256);
@@ -418,7 +444,7 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
         return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus)
+    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true)
                              : down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
     DownParams dp{};
     dp.down = mat_dev(ffn->down);
@@ -505,7 +531,7 @@ RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k)
 {
     RoutedWs w{};
     const size_t P = (size_t)m * k;
-    const int kg = down_ranges(fmt, moe_inter, hidden, m);
+    const int kg = down_ranges(fmt, moe_inter, hidden, m, false);
     size_t o = 0;
     w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
@@ -674,7 +700,7 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     // phase 2: down per union entry and tile, d_p to pair_out
-    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus)
+    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false)
                              : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
     DownParams dp{};
     dp.down = mat_dev(experts->down);

@@ -263,7 +263,9 @@ struct RegStager {
 #pragma unroll
         for (int i = 0; i < kSR; ++i) *(u32x4*)(L.x + (size_t)slot[i] * 16) = v[i];
     }
-    // all batches but the last, then the last batch's loads
+    // all batches but the last, then the last batch's loads.  The K range must
+    // not be empty (per_row > 0): the host never splits K into more ranges than
+    // it has K units.
     __device__ __forceinline__ void begin()
     {
         const int step = kSR * nthr;
@@ -528,9 +530,14 @@ __device__ __forceinline__ void tiled_stream(Ring& ring, int kb0, const Lds& L, 
 // blockIdx.x, +gridDim.x, ...; consecutive units of the same item form a run,
 // for which the activation rows stay staged and the ring runs on from tile to
 // tile.  Grid row blockIdx.y takes a range of K (whole scale/zero groups for
-// INT4, blocks for INT8), and the KS waves of the workgroup split that range.
-// At each tile end the waves' partial sums meet in LDS (double-buffered by tile
-// parity) and the tile's outputs are finished.
+// INT4, blocks for INT8).  Two ways to share it among the KS waves:
+//   K split (!TS): the waves split the K range of every tile; at each
+//     tile end their partial sums meet in LDS (double-buffered by tile parity)
+//     and the tile's outputs are finished.
+//   tile split (TS): every wave covers the whole K range and the waves
+//     take turns over the run's tiles; each wave finishes its own tiles from
+//     its accumulators, with no reduction or barrier.  The staged activation
+//     rows then serve KS tiles at once.
 //
 // HILO: the staged rows are hi/lo pairs of one activation row (the down
 // projection): row 2r + 1 is added to row 2r before the finish.
@@ -553,7 +560,7 @@ struct TiledJob {
     int KS, G;                // waves per workgroup, gridDim.x
 };
 
-template <int FMT, int NMAT, int NT, int MT, bool HILO, typename Rows, typename Finish>
+template <int FMT, int NMAT, int NT, int MT, bool HILO, bool TS, typename Rows, typename Finish>
 __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish finish)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -569,7 +576,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
     const int U0 = nun * (int)blockIdx.y / J.KG, U1 = nun * ((int)blockIdx.y + 1) / J.KG;
     const int kb0 = FMT == FMT_INT4 ? 8 * U0 : U0;
     const int kb1 = FMT == FMT_INT4 ? min(8 * U1, geo.nbk) : U1;
-    const int u0w = U0 + (U1 - U0) * w / KS, u1w = U0 + (U1 - U0) * (w + 1) / KS;
+    const int u0w = TS ? U0 : U0 + (U1 - U0) * w / KS, u1w = TS ? U1 : U0 + (U1 - U0) * (w + 1) / KS;
     const int s0 = FMT == FMT_INT4 ? 9 * u0w : u0w;
     const int s1 = FMT == FMT_INT4 ? min(9 * u1w, geo.steps) : u1w;
 
@@ -591,11 +598,15 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt) eq[mt] = J.tq[mt] + (size_t)it.e * J.tebytes;
             const int t0 = u0 - item * T;   // tile of the run's first unit; later ones are G tiles apart
-            auto base = [&](int i, int mt) { return eq[mt] + (size_t)(t0 + i * G) * geo.tile_bytes; };
+            // this wave's units of the run: all (K split) or w, w + KS, ... (tile split)
+            const int wi0 = TS ? w : 0, wstep = TS ? KS : 1;
+            const int nrun = TS ? (run > w ? (run - w + KS - 1) / KS : 0) : run;
+            auto tile_at = [&](int i) { return t0 + (wi0 + i * wstep) * G; };
+            auto base = [&](int i, int mt) { return eq[mt] + (size_t)tile_at(i) * geo.tile_bytes; };
             const int RR = J.rows_per_item_mul * it.R;
             for (int c0 = 0; c0 < RR; c0 += J.rows_cap) {
-                TRing<NMAT, kPfT, decltype(base)> ring(base, run, s0, s1);
-                const TLdsLayout LL = tiled_launch_lds(NMAT, FMT, J.N, J.K, J.KG, J.rows_cap, KS, PER * RL);
+                TRing<NMAT, kPfT, decltype(base)> ring(base, nrun, s0, s1);
+                const TLdsLayout LL = tiled_launch_lds(NMAT, FMT, J.N, J.K, J.KG, J.rows_cap, KS, TS ? 0 : PER * RL);
                 Lds L;
                 L.x = smem;
                 L.per_row = (kb1 - kb0) * (FmtT<FMT>::BK / 8);
@@ -610,8 +621,55 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
                 const size_t red_half = (size_t)KS * PER * RL;
                 const int Rc = min(J.rows_cap, RR - c0);
                 auto end = [&](int i, f32x4 (&tot)[NMAT][NT], f32x4 (&one)[NT]) {
-                    const int tile = t0 + i * G;
+                    const int tile = tile_at(i);
                     const int row0 = tile * 16;
+                    if constexpr (TS) {   // this wave's own tile: finish from the accumulators
+                        constexpr int MTC = (NT == 1) ? MT : 4;
+                        const int l16 = lane >> 4, nl = lane & 15, n = row0 + nl;
+                        float sc[NMAT];
+#pragma unroll
+                        for (int mt = 0; mt < NMAT; ++mt)
+                            sc[mt] = FMT == FMT_INT8 ? tile_row_scale(eq[mt] + geo.scale_off + (size_t)tile * 64, nl) : 1.0f;
+                        if (n < J.N) {
+#pragma unroll
+                            for (int tb = 0; tb < NT; ++tb) {
+                                if constexpr (HILO) {
+#pragma unroll
+                                    for (int h2 = 0; h2 < 2; ++h2) {
+                                        const int xr = tb * 16 + 4 * l16 + 2 * h2;   // hi row of a hi/lo pair
+                                        if (xr >= Rc) continue;
+                                        const int orow = orows[xr >> 1];
+                                        if (orow < 0) continue;
+                                        float vh = tot[0][tb][2 * h2], vl = tot[0][tb][2 * h2 + 1];
+                                        if constexpr (FMT == FMT_INT8) {
+                                            vh = fmaf(-128.0f, one[tb][2 * h2], vh);
+                                            vl = fmaf(-128.0f, one[tb][2 * h2 + 1], vl);
+                                        }
+                                        float v[NMAT];
+                                        v[0] = sc[0] * (vh + vl);
+                                        finish(orow, n, v);
+                                    }
+                                } else {
+#pragma unroll
+                                    for (int i2 = 0; i2 < MTC; ++i2) {
+                                        const int xr = tb * 16 + 4 * l16 + i2;
+                                        if (xr >= Rc) continue;
+                                        const int orow = orows[xr];
+                                        if (orow < 0) continue;
+                                        float v[NMAT];
+#pragma unroll
+                                        for (int mt = 0; mt < NMAT; ++mt) {
+                                            float h = tot[mt][tb][i2];
+                                            if constexpr (FMT == FMT_INT8) h = fmaf(-128.0f, one[tb][i2], h);
+                                            v[mt] = sc[mt] * h;
+                                        }
+                                        finish(orow, n, v);
+                                    }
+                                }
+                            }
+                        }
+                        return;
+                    }
                     float* rb = red + (size_t)(i & 1) * red_half;
 #pragma unroll
                     for (int tb = 0; tb < NT; ++tb) {
@@ -702,7 +760,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
 // values, and what the compiler knows of the pointers, are unchanged.  The
 // launch shape comes in the arguments too (ks, grid) rather than from the
 // dispatch packet.
-template <int FMT, int NT, int MT>
+template <int FMT, int NT, int MT, bool TS>
 __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
 {
     asm volatile("" ::"s"(p.tgate), "s"(p.tup), "s"(p.tebytes), "s"(p.N), "s"(p.K), "s"(p.x), "s"(p.rows_cap),
@@ -749,7 +807,7 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
         act_out[o] = hi;
         act_out[o + J.N] = lo;
     };
-    tiled_body<FMT, 2, NT, MT, false>(J, rows, finish);
+    tiled_body<FMT, 2, NT, MT, false, TS>(J, rows, finish);
     // shared-expert gate logits (read by the down kernel's tail): one
     // workgroup, after its tiles
     if (gate_vec != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
@@ -766,7 +824,7 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
 
 // down + tail: h per (token or pair, hidden row), finished by down_finish
 // (tail, or fp32 partials when K is split or for the routed and RMSNorm tails).
-template <int FMT, int NT, int MT>
+template <int FMT, int NT, int MT, bool TS>
 __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
 {
     asm volatile("" ::"s"(p.tdown), "s"(p.tebytes), "s"(p.N), "s"(p.K), "s"(p.KG), "s"(p.act), "s"(p.rows_cap),
@@ -799,7 +857,7 @@ __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
         if ((t & 1) == 0) orows[t >> 1] = arow;
     };
     auto finish = [&](int orow, int n, const float (&v)[1]) { down_finish(p, orow, n, v[0]); };
-    tiled_body<FMT, 1, NT, MT, true>(J, rows, finish);
+    tiled_body<FMT, 1, NT, MT, true, TS>(J, rows, finish);
 }
 
 }  // namespace ffnq
