@@ -188,6 +188,119 @@ def run_phases(m: int, steps: int, warmup: int, copies: int, tiled: bool = True)
     return d.mean(axis=0), gu_bytes(c["hidden"], c["inter"], c["fmt"], m)
 
 
+# Steady-state timing of every workload shape: weight copies rotated so that the
+# bytes a call touches, over all copies, exceed twice the 256 MB Infinity Cache
+# (the 256x704 INT8 layer is L2-resident whatever is done, and is reported as a
+# latency).  Routed layers time the whole layer: shared expert (config 3),
+# router top-k and plan, routed phases 1 and 2.
+CONFIG_COPIES = {0: 1, 2: 6, 3: 6}
+
+
+def _clone_mats(d: dict) -> dict:
+    import torch
+    return {n: {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in m.items()} for n, m in d.items()}
+
+
+def _dev16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
+    import torch
+    import gen
+    import moe_expert_dequant_amd as fq
+
+    cfg = gen.CONFIGS[c]
+    inp = gen.config_inputs(c, m)
+    hidden = cfg["hidden"]
+    ws = fq.Workspace()
+    x = _dev16(inp["x"])
+    resid = _dev16(inp["resid"])
+    if cfg["kind"] in ("dense", "shared"):
+        inter = cfg["inter"]
+        base = {n: fq.pack(fq.to_device(inp["ffn"][n])) for n in ("gate", "up", "down")}
+        copies = CONFIG_COPIES.get(c, 6)
+        layers = [base] + [_clone_mats(base) for _ in range(copies - 1)]
+        structs = [fq.ffn_struct(d) for d in layers]
+        wbytes = 2 * weight_bytes(cfg["fmt"], inter, hidden) + weight_bytes(cfg["fmt"], hidden, inter)
+        if cfg["kind"] == "dense":
+            io = 2 * m * hidden + 4 * m * hidden                          # x; residual read and written
+            call = lambda i: fq.dense(structs[i % copies], hidden, inter, m, cfg["act"], cfg["tail"], x, resid, ws=ws)
+        else:
+            out = torch.zeros((m, hidden), dtype=torch.int16, device="cuda")
+            nw = _dev16(inp["norm_w"])
+            io = 2 * m * hidden + 2 * m * hidden + 2 * hidden            # x; norm output; norm weight
+            call = lambda i: fq.shared_expert(structs[i % copies], hidden, inter, m, cfg["act"], cfg["tail"], x, out,
+                                              nw, cfg["eps"], ws=ws)
+        extra = {}
+        bytes_of = lambda: wbytes + io
+    else:
+        E, inter, k, cap = cfg["n_experts"], cfg["moe_inter"], cfg["top_k"], cfg["cap"]
+        ex = {n: fq.pack(fq.to_device(inp["experts"][n]), E) for n in ("gate", "up", "down")}
+        ebytes = 2 * weight_bytes(cfg["fmt"], inter, hidden) + weight_bytes(cfg["fmt"], hidden, inter)
+        sh = None
+        if cfg["shared_inter"]:
+            sh = {n: fq.pack(fq.to_device(inp["shared"][n])) for n in ("gate", "up", "down")}
+        logits = torch.from_numpy(np.ascontiguousarray(inp["logits"], dtype=np.float32)).cuda()
+        ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+        w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+        plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+        fq.moe_route(logits, m, E, k, cap, ids, w, plan)
+        torch.cuda.synchronize()
+        p = plan.cpu().numpy()
+        n_sub = min(max(int(p[0]), 0), m)
+        union = min(max(int(p[m + 2 + n_sub]), 0), m * k)           # union entries of all sub-batches
+        touched = union * ebytes + (0 if sh is None else 2 * weight_bytes(cfg["fmt"], cfg["shared_inter"], hidden)
+                                    + weight_bytes(cfg["fmt"], hidden, cfg["shared_inter"]))
+        copies = max(2, -(-2 * 256 * 1000 * 1000 // max(touched, 1)))
+        exs = [ex] + [_clone_mats(ex) for _ in range(copies - 1)]
+        ex_st = [fq.ffn_struct(d) for d in exs]
+        shs = None if sh is None else [fq.ffn_struct(d) for d in ([sh] + [_clone_mats(sh) for _ in range(copies - 1)])]
+        seed = torch.zeros((m, hidden), dtype=torch.int16, device="cuda") if sh is not None else None
+        gv = _dev16(inp["gate_vec"]) if sh is not None else None
+        ws2 = fq.Workspace()
+
+        def call(i):
+            if shs is not None:
+                fq.shared_expert(shs[i % copies], hidden, cfg["shared_inter"], m, cfg["act"], gen.TAIL_SIGMOID_GATE,
+                                 x, seed, gv, ws=ws2)
+            fq.moe_route(logits, m, E, k, cap, ids, w, plan)
+            fq.moe_routed_batched(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"], x, ids, w, plan, seed, resid,
+                                  ws=ws)
+        counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
+        extra = dict(union=union, sub_batches=n_sub, tokens_per_expert_min=int(counts[counts > 0].min()),
+                     tokens_per_expert_max=int(counts.max()))
+        io = 2 * m * hidden + 4 * m * E + 4 * m * hidden                 # x; logits; residual read and written
+        bytes_of = lambda: touched + io
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        st[i].record()
+        call(i)
+        en[i].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in zip(st, en)]) * 1e-3   # s
+    med = float(np.median(t))
+    nb = bytes_of()
+    return dict(call_us_median=med * 1e6, call_us_p10=float(np.percentile(t, 10)) * 1e6,
+                call_us_p90=float(np.percentile(t, 90)) * 1e6, tokens_per_s=m / med, bytes_per_call=nb,
+                achieved_GBs=nb / med / 1e9, frac_of_peak=nb / med / 1e9 / HBM_PEAK_GBS, weight_copies=copies, **extra)
+
+
+def run_configs(steps: int, warmup: int) -> dict:
+    import gen
+    out = {}
+    for c in sorted(gen.CONFIGS):
+        cfg = gen.CONFIGS[c]
+        out[cfg["name"]] = {f"M={m}": run_config(c, m, steps, warmup) for m in cfg["ms"]}
+        print(f"# config {c} done", file=sys.stderr, flush=True)
+    return out
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -230,6 +343,7 @@ def main():
     ap.add_argument("--single", action="store_true", help="time only --m, headline pass only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--rowmajor", action="store_true", help="stream the row-major weights instead of the tiled ones")
+    ap.add_argument("--no-configs", action="store_true", help="skip the steady-state timing of every workload shape")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is a "
@@ -307,6 +421,8 @@ def main():
                              "frac_of_peak": r["bytes"] / r["avg_s"] / 1e9 / HBM_PEAK_GBS,
                              **({k: v for k, v in phases[m].items()} if m in phases else {})}
                     for m, r in res.items()}
+    if not (args.no_configs or args.single):
+        out["configs"] = run_configs(100, 10)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
