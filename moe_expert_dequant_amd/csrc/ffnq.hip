@@ -22,6 +22,18 @@ namespace {
 using namespace ffnq;
 
 constexpr size_t kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
+constexpr size_t kLdsBig = 152 * 1024;     // one workgroup per CU (prefill-sized items)
+constexpr int kBigRows = 12;               // activation rows per item from which the prefill shapes apply
+
+// Rows per work item: every token (dense), or the pairs of one expert of the
+// union on average (routed; the union is at most min(pairs, experts)).
+int rows_per_item(bool dense, int m, int top_k, int n_experts)
+{
+    if (dense) return m;
+    const long long P = (long long)m * top_k;
+    const long long u = std::max<long long>(1, std::min<long long>(P, n_experts));
+    return (int)((P + u - 1) / u);
+}
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -250,11 +262,29 @@ int tiled_ks(int units, long long tiles_total, int cus, int per_cu, int max_ks)
     return (units + per - 1) / per;
 }
 
-KConfig gu_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus)
+KConfig gu_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus, int rows_item)
 {
     KConfig c{};
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
+    if (rows_item >= kBigRows) {
+        // prefill-sized items: one 16-row block per pass with the whole K range of
+        // its rows staged (one workgroup per CU), the waves splitting K, and one
+        // resident workgroup per CU so that each walks runs of tiles of an item
+        const int nun = is_int4(fmt) ? geo.ng : geo.nbk;
+        c.nt = 1;
+        c.mt = 4;
+        c.rows_cap = std::min(std::max(1, rows_total), 16);
+        c.kg = 1;
+        c.ks = is_int4(fmt) ? std::min(nun, 8) : std::max(1, std::min(8, nun / 4));
+        for (;;) {
+            c.lds = tiled_launch_lds(2, F, N, K, 1, c.rows_cap, c.ks, 2 * c.nt * 4 * red_lanes(c.nt, c.rows_cap)).total;
+            if (c.lds <= kLdsBig || c.rows_cap <= 1) break;
+            --c.rows_cap;
+        }
+        c.grid = (int)std::max<long long>(1, std::min<long long>(items_est * geo.T, (long long)cus));
+        return c;
+    }
     const int nun = is_int4(fmt) ? geo.ng : geo.nbk;
     const int rp = std::max(1, std::min(rows_total, 32));
     c.nt = rp <= 16 ? 1 : 2;
@@ -285,7 +315,7 @@ struct DSplit {
     int kg, ks, rows_cap, nt, ts, gx;
 };
 
-DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense)
+DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int rows_item)
 {
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
@@ -307,7 +337,17 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense)
     } else {
         d.ks = std::max(1, std::min(8, upw / 4));
     }
-    if (dense && rows_total >= 2) {
+    if (!dense && rows_item >= kBigRows) {
+        // prefill-sized routed items: tile split over runs of 8 tiles of one item
+        // (gx = T/8 workgroups along x walk the union), the staged rows' K range
+        // sized to fill one workgroup per CU
+        d.ts = 1;
+        d.ks = 8;
+        d.gx = (geo.T + d.ks - 1) / d.ks;
+        int tk = 1;
+        while (tk < nun && tiled_launch_lds(1, F, N, K, tk, d.rows_cap, d.ks, 0).total > kLdsBig) ++tk;
+        d.kg = tk;
+    } else if (dense && rows_total >= 2) {
         d.ts = 1;
         d.ks = 4;
         d.gx = (geo.T + d.ks - 1) / d.ks;
@@ -320,9 +360,10 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense)
     return d;
 }
 
-KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus, bool dense)
+KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus, bool dense,
+                          int rows_item)
 {
-    const DSplit d = down_tiled_split(fmt, K, N, rows_total, dense);
+    const DSplit d = down_tiled_split(fmt, K, N, rows_total, dense, rows_item);
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
     KConfig c{};
@@ -379,9 +420,10 @@ bool launch_down_tiled(int fmt, const KConfig& c, hipStream_t stream, const Down
 }
 
 // K ranges of the down projection for a format (row-major or tiled).
-int down_ranges(int fmt, int K, int N, int rows_total, bool dense)
+int down_ranges(int fmt, int K, int N, int rows_total, bool dense, int rows_item)
 {
-    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total, dense).kg : down_kg(fmt, K, N, rows_total);
+    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total, dense, rows_item).kg
+                         : down_kg(fmt, K, N, rows_total);
 }
 
 // ---------------------------------------------------------------------------
@@ -395,7 +437,7 @@ DenseWs dense_ws(int fmt_down, int hidden, int inter, int m)
 {
     DenseWs w{};
     size_t o = 0;
-    const int kg = down_ranges(fmt_down, inter, hidden, m, true);
+    const int kg = down_ranges(fmt_down, inter, hidden, m, true, m);
     w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * m * hidden * sizeof(float), 256);
     w.logit = o; o += align_up((size_t)m * sizeof(float), 256);
@@ -412,7 +454,7 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
     const int gfmt = to_fmt(ffn->gate.fmt), dfmt = to_fmt(ffn->down.fmt);
 
     const bool tiled = is_tiled(ffn->gate.fmt);
-    const KConfig gc = tiled ? gu_tiled_config(ffn->gate.fmt, hidden, inter, 1, m, cus)
+    const KConfig gc = tiled ? gu_tiled_config(ffn->gate.fmt, hidden, inter, 1, m, cus, m)
                              : gu_config(ffn->gate.fmt, hidden, inter, 1, m, cus);
     GUParams gp{};
     gp.gate = mat_dev(ffn->gate);
@@ -441,7 +483,7 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
         return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true)
+    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true, m)
                              : down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
     DownParams dp{};
     dp.down = mat_dev(ffn->down);
@@ -471,7 +513,9 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     if (tail == FFNQ_TAIL_RMSNORM) {
-        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), 0, stream, dp.part, dc.kg, m, aux, out, hidden, eps);
+        const size_t row_lds = hidden <= kRowLds ? (size_t)hidden * 6 : 0;
+        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), row_lds, stream, dp.part, dc.kg, m, aux, out, hidden,
+                           eps);
         if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
     } else if (dc.kg > 1) {
         const long long total = (long long)m * hidden;
@@ -524,11 +568,11 @@ struct RoutedWs {
     size_t act, part, total;
 };
 
-RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k)
+RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k, int n_experts)
 {
     RoutedWs w{};
     const size_t P = (size_t)m * k;
-    const int kg = down_ranges(fmt, moe_inter, hidden, m, false);
+    const int kg = down_ranges(fmt, moe_inter, hidden, m, false, rows_per_item(false, m, k, n_experts));
     size_t o = 0;
     w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
@@ -652,7 +696,7 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
     const size_t rows_bytes = (size_t)m * hidden * 2;
     if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
-    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k);
+    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
     if (!ws) {
         *ws_bytes = L.total;
         return FFNQ_OK;
@@ -668,7 +712,8 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
 
     // phase 1: gate/up + activation per union entry and tile
     const bool tiled = is_tiled(experts->gate.fmt);
-    const KConfig gc = tiled ? gu_tiled_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus)
+    const KConfig gc = tiled ? gu_tiled_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus,
+                                               rows_per_item(false, m, top_k, n_experts))
                              : gu_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus);
     GUParams gp{};
     gp.gate = mat_dev(experts->gate);
@@ -697,7 +742,8 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     // phase 2: down per union entry and tile, d_p to pair_out
-    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false)
+    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false,
+                                                 rows_per_item(false, m, top_k, n_experts))
                              : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
     DownParams dp{};
     dp.down = mat_dev(experts->down);

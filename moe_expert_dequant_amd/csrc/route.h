@@ -14,6 +14,7 @@ namespace ffnq {
 
 constexpr int kMaxExperts = 1024;   // logits per token held in registers: 16 per lane
 constexpr int kMaxSlots = 32;
+constexpr int kIdsCache = 4096;      // pairs whose expert ids the plan pass reads from LDS
 
 struct RouteParams {
     const float* logits;    // [m][E]
@@ -48,9 +49,13 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 {
     __shared__ int slot_of[kMaxExperts];
     __shared__ int cur_union[kMaxSlots];
+    __shared__ int ids_s[kIdsCache];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
     const int m = p.m, k = p.k, E = p.E;
     const int nj = (E + 63) >> 6;
+    // the plan pass reads the chosen experts back: from LDS when they fit
+    const bool cached = (long long)m * k <= kIdsCache;
+    auto id_of = [&](int pp) { return cached ? ids_s[pp] : p.ids[pp]; };
 
     // ---- top-k and weights, one token per wave ----
     for (int t = w; t < m; t += nw) {
@@ -84,6 +89,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
             const double sc = p.scale ? (double)p.scale[my_e] : 1.0;
             p.ids[(size_t)t * k + lane] = my_e;
             p.w[(size_t)t * k + lane] = (float)(ex / sum * sc);
+            if (cached) ids_s[t * k + lane] = my_e;
         }
     }
 
@@ -114,7 +120,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
         int cnt = 0;   // lane j < usize: pairs in slot j
         for (int c = P0; c < P1; c += 64) {
             const int pp = c + lane;
-            const int sl = (pp < P1) ? slot_of[p.ids[pp]] : -1;
+            const int sl = (pp < P1) ? slot_of[id_of(pp)] : -1;
             for (int j = 0; j < usize; ++j) {
                 const uint64_t msk = __ballot(sl == j);
                 if (lane == j) cnt += __popcll(msk);
@@ -130,7 +136,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
         if (lane < usize) spb[base + lane] = cur;
         for (int c = P0; c < P1; c += 64) {
             const int pp = c + lane;
-            const int sl = (pp < P1) ? slot_of[p.ids[pp]] : -1;
+            const int sl = (pp < P1) ? slot_of[id_of(pp)] : -1;
             for (int j = 0; j < usize; ++j) {
                 const uint64_t msk = __ballot(sl == j);
                 const int start = __shfl(cur, j);
@@ -146,7 +152,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     };
 
     for (int t = 0; t < m; ++t) {
-        const int e = (lane < k) ? p.ids[(size_t)t * k + lane] : 0;
+        const int e = (lane < k) ? id_of(t * k + lane) : 0;
         int cur = (lane < k) ? slot_of[e] : 0;
         bool fresh = (lane < k) && cur < 0;
         uint64_t fm = __ballot(fresh);

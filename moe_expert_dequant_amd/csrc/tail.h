@@ -7,19 +7,36 @@
 namespace ffnq {
 
 // part[0] + part[1] + ... + part[R-1] at idx, added in that order.  The loads
-// go out in batches of 8 before the adds, so a batch costs one memory latency
+// go out in batches of 8 before the adds (a batch past R re-reads the last
+// range, and its values are not added), so a batch costs one memory latency
 // rather than one per range.
 __device__ __forceinline__ float sum_parts(const float* part, int R, size_t stride, size_t idx)
 {
-    float h = 0.0f;
-    for (int r0 = 0; r0 < R; r0 += 8) {
-        float v[8];
+    float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = r0 + j < R ? part[(size_t)(r0 + j) * stride + idx] : 0.0f;
+    for (int j = 0; j < 8; ++j) v[j] = part[(size_t)min(j, R - 1) * stride + idx];   // R >= 1
+    float h = v[0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (r0 + j < R) h = r0 + j == 0 ? v[j] : h + v[j];
+    for (int j = 1; j < 8; ++j) h = j < R ? h + v[j] : h;
+    for (int r0 = 8; r0 < R; r0 += 8) {   // more than 8 ranges: further batches
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = part[(size_t)min(r0 + j, R - 1) * stride + idx];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h = r0 + j < R ? h + v[j] : h;
     }
+    return h;
+}
+
+// sum_parts for 1 <= R <= 8: one batch, no loop, so that a caller's unrolled
+// loop over elements can put several elements' loads in flight together.
+__device__ __forceinline__ float sum_parts8(const float* part, int R, size_t stride, size_t idx)
+{
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = part[(size_t)min(j, R - 1) * stride + idx];
+    float h = v[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) h = j < R ? h + v[j] : h;
     return h;
 }
 
@@ -27,18 +44,57 @@ __device__ __forceinline__ float sum_parts(const float* part, int R, size_t stri
 //   out[t][i] = bf16(h[t][i] / sqrt(mean_i h^2 + eps) * w[i])
 // ([gemma4/shared_expert.rs] encode_rms_norm_bf16w with RMS_EPS).  The sum
 // of squares, the scale and the product are formed in double; the result is
-// rounded to bf16 once.  One workgroup per row.
+// rounded to bf16 once.  One workgroup per row.  With `held` (rows of at most
+// kRowLds values) the summed row and the weight are kept in dynamic LDS between
+// the two passes, loaded together in the first; the host launches with n * 6
+// bytes of LDS then.
+constexpr int kRowLds = 8192;
+
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ part, int R, int m,
                                                       const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
                                                       int n, float eps)
 {
+    extern __shared__ float hrow[];   // [n] summed row, then [n] bf16 weight
+    uint16_t* wrow = (uint16_t*)(hrow + n);
     __shared__ double partial[256 / 64];
     const int t = blockIdx.x, tid = threadIdx.x;
     const size_t stride = (size_t)m * n;
+    const bool held = n <= kRowLds;
     double ss = 0.0;
-    for (int i = tid; i < n; i += blockDim.x) {
-        const double h = sum_parts(part, R, stride, (size_t)t * n + i);
-        ss += h * h;
+    if (held && R <= 8) {
+        // four elements per step, their loads together (indices clamped into
+        // the row; only elements < n are kept), added to ss in element order
+        for (int i0 = tid; i0 < n; i0 += 4 * 256) {
+            float h4[4];
+            uint16_t w4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ic = min(i0 + 256 * u, n - 1);
+                h4[u] = sum_parts8(part, R, stride, (size_t)t * n + ic);
+                w4[u] = w[ic];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + 256 * u;
+                if (i < n) {
+                    hrow[i] = h4[u];
+                    wrow[i] = w4[u];
+                    ss += (double)h4[u] * (double)h4[u];
+                }
+            }
+        }
+    } else if (held) {
+        for (int i = tid; i < n; i += blockDim.x) {
+            const float h = sum_parts(part, R, stride, (size_t)t * n + i);
+            hrow[i] = h;
+            wrow[i] = w[i];
+            ss += (double)h * (double)h;
+        }
+    } else {
+        for (int i = tid; i < n; i += blockDim.x) {
+            const float h = sum_parts(part, R, stride, (size_t)t * n + i);
+            ss += (double)h * (double)h;
+        }
     }
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     if ((tid & 63) == 0) partial[tid >> 6] = ss;
@@ -47,8 +103,9 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += partial[i];
     const double r = 1.0 / sqrt(tot / (double)n + (double)eps);
     for (int i = tid; i < n; i += blockDim.x) {
-        const double h = sum_parts(part, R, stride, (size_t)t * n + i);
-        out[(size_t)t * n + i] = bf16_from_f64(h * r * (double)bf16_f32(w[i]));
+        const double h = held ? (double)hrow[i] : (double)sum_parts(part, R, stride, (size_t)t * n + i);
+        const uint16_t wi = held ? wrow[i] : w[i];
+        out[(size_t)t * n + i] = bf16_from_f64(h * r * (double)bf16_f32(wi));
     }
 }
 
