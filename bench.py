@@ -344,6 +344,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--rowmajor", action="store_true", help="stream the row-major weights instead of the tiled ones")
     ap.add_argument("--no-configs", action="store_true", help="skip the steady-state timing of every workload shape")
+    ap.add_argument("--config", type=int, default=None,
+                    help="time only workload shape CONFIG at --m tokens (steady state; for kernel traces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is a "
@@ -356,6 +358,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.config is not None:
+        r = run_config(args.config, args.m, args.steps, args.warmup)
+        print(json.dumps({"config": args.config, "m": args.m, **r}), flush=True)
         return
 
     res = {}
