@@ -252,11 +252,13 @@ bool launch_down(int fmt, const KConfig& c, long long items, int N, hipStream_t 
 // tiled kernels: configuration and dispatch
 
 // Waves per workgroup splitting a tile's K units (scale/zero groups or
-// blocks): enough waves in flight per CU (about `per_cu`) while every wave
-// keeps the smallest possible number of units, all waves equal if possible.
+// blocks): about `per_cu` waves per CU, not more (rounded down: a grid of one
+// workgroup per tile that overflows the resident waves leaves a second
+// generation to start late), while every wave keeps the smallest possible
+// number of units, all waves equal if possible.
 int tiled_ks(int units, long long tiles_total, int cus, int per_cu, int max_ks)
 {
-    long long want = ((long long)cus * per_cu + tiles_total - 1) / std::max<long long>(1, tiles_total);
+    long long want = ((long long)cus * per_cu) / std::max<long long>(1, tiles_total);
     int ks = (int)std::max<long long>(1, std::min<long long>({want, (long long)units, (long long)max_ks}));
     const int per = (units + ks - 1) / ks;
     return (units + per - 1) / per;
