@@ -129,6 +129,31 @@ __global__ void __launch_bounds__(256) ksum_tail_kernel(const float* __restrict_
     }
 }
 
+// Ranks of one token in batches of KB: the batch's ids, weights and partials
+// are loaded before any add (ranks past k re-read rank k-1 and are not added);
+// the adds keep rank order.
+template <int KB>
+__device__ __forceinline__ float moe_ranks(const float* __restrict__ part, int R, size_t stride,
+                                           const float* __restrict__ topk_w, const int32_t* __restrict__ topk_ids,
+                                           int n_experts, int t, int k, int n, int i, float acc)
+{
+    for (int r0 = 0; r0 < k; r0 += KB) {
+        int e[KB];
+        float wt[KB], d[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const int p = t * k + min(r0 + j, k - 1);
+            e[j] = topk_ids[p];
+            wt[j] = topk_w[p];
+            d[j] = R <= 8 ? sum_parts8(part, R, stride, (size_t)p * n + i) : sum_parts(part, R, stride, (size_t)p * n + i);
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+            if (r0 + j < k && e[j] >= 0 && e[j] < n_experts) acc = __fadd_rn(acc, __fmul_rn(wt[j], d[j]));
+    }
+    return acc;
+}
+
 // The seeded phase-2 reduction and the raw residual add of the routed half
 // ([qwen/moe_batch.rs]: moe_phase2_down_reduce_k8 starts its fp32
 // accumulator at the gated shared expert, then adds the ranks in order; the
@@ -146,14 +171,14 @@ __global__ void __launch_bounds__(256) moe_reduce_kernel(const float* __restrict
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
         const int t = (int)(idx / n), i = (int)(idx - (size_t)t * n);
         float acc = seed ? bf16_f32(seed[idx]) : 0.0f;
-        for (int r = 0; r < k; ++r) {
-            const int p = t * k + r;
-            const int e = topk_ids[p];
-            if (e < 0 || e >= n_experts) continue;
-            const float d = sum_parts(part, R, stride, (size_t)p * n + i);
-            acc = __fadd_rn(acc, __fmul_rn(topk_w[p], d));
-        }
-        resid[idx] = bf16_from_f64((double)bf16_f32(resid[idx]) + (double)acc);
+        const float rs = bf16_f32(resid[idx]);
+        if (k <= 2)
+            acc = moe_ranks<2>(part, R, stride, topk_w, topk_ids, n_experts, t, k, n, i, acc);
+        else if (k <= 4)
+            acc = moe_ranks<4>(part, R, stride, topk_w, topk_ids, n_experts, t, k, n, i, acc);
+        else
+            acc = moe_ranks<8>(part, R, stride, topk_w, topk_ids, n_experts, t, k, n, i, acc);
+        resid[idx] = bf16_from_f64((double)rs + (double)acc);
     }
 }
 
