@@ -15,6 +15,7 @@ namespace ffnq {
 constexpr int kMaxExperts = 1024;   // logits per token held in registers: 16 per lane
 constexpr int kMaxSlots = 32;
 constexpr int kIdsCache = 4096;      // pairs whose expert ids the plan pass reads from LDS
+constexpr int kRankMax = 256;        // experts up to which the top-k is found by ranking in LDS
 
 struct RouteParams {
     const float* logits;    // [m][E]
@@ -50,6 +51,8 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     __shared__ int slot_of[kMaxExperts];
     __shared__ int cur_union[kMaxSlots];
     __shared__ int ids_s[kIdsCache];
+    __shared__ uint64_t keys_s[256 / 64][kRankMax];   // per wave: the token's keys
+    __shared__ int sel_s[256 / 64][kRankMax];         // per wave: expert of each rank < k
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
     const int m = p.m, k = p.k, E = p.E;
     const int nj = (E + 63) >> 6;
@@ -66,15 +69,39 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
             key[j] = (j < nj && e < E) ? route_key(p.logits[(size_t)t * E + e], e) : 0ull;
         }
         int my_e = -1;
-        for (int r = 0; r < k; ++r) {
-            uint64_t best = 0;
+        if (E <= kRankMax) {
+            // rank of each key = number of keys above it (keys are distinct: they
+            // carry the index); the keys of ranks 0..k-1 are the top k in order
 #pragma unroll
-            for (int j = 0; j < kMaxExperts / 64; ++j) best = key[j] > best ? key[j] : best;
-            best = wave_max_u64(best);
+            for (int j = 0; j < kRankMax / 64; ++j)
+                if (lane + 64 * j < E) keys_s[w][lane + 64 * j] = key[j];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            int rank[kRankMax / 64] = {};
+            for (int q = 0; q < E; ++q) {
+                const uint64_t o = keys_s[w][q];
 #pragma unroll
-            for (int j = 0; j < kMaxExperts / 64; ++j)
-                if (key[j] == best) key[j] = 0ull;
-            if (lane == r) my_e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+                for (int j = 0; j < kRankMax / 64; ++j) rank[j] += o > key[j] ? 1 : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kRankMax / 64; ++j)
+                if (lane + 64 * j < E && rank[j] < k) sel_s[w][rank[j]] = lane + 64 * j;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (lane < k) my_e = sel_s[w][lane];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();   // the next token's writes come after these reads
+        } else {
+            for (int r = 0; r < k; ++r) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int j = 0; j < kMaxExperts / 64; ++j) best = key[j] > best ? key[j] : best;
+                best = wave_max_u64(best);
+#pragma unroll
+                for (int j = 0; j < kMaxExperts / 64; ++j)
+                    if (key[j] == best) key[j] = 0ull;
+                if (lane == r) my_e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+            }
         }
         double lr = -INFINITY;
         if (lane < k) {
