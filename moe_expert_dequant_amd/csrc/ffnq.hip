@@ -340,12 +340,12 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int r
         d.ks = std::max(1, std::min(8, upw / 4));
     }
     if (!dense && rows_item >= kBigRows) {
-        // prefill-sized routed items: tile split over runs of 8 tiles of one item
-        // (gx = T/8 workgroups along x walk the union), the staged rows' K range
-        // sized to fill one workgroup per CU
+        // prefill-sized routed items: tile split over runs of 16 tiles of one item
+        // (2 per wave; gx = T/16 workgroups along x walk the union), the staged
+        // rows' K range sized to fill one workgroup per CU
         d.ts = 1;
         d.ks = 8;
-        d.gx = (geo.T + d.ks - 1) / d.ks;
+        d.gx = (geo.T + 2 * d.ks - 1) / (2 * d.ks);
         int tk = 1;
         while (tk < nun && tiled_launch_lds(1, F, N, K, tk, d.rows_cap, d.ks, 0).total > kLdsBig) ++tk;
         d.kg = tk;
