@@ -317,7 +317,7 @@ struct DSplit {
     int kg, ks, rows_cap, nt, ts, gx;
 };
 
-DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int rows_item)
+DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int rows_item, bool tail_sums)
 {
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
@@ -349,7 +349,9 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int r
         int tk = 1;
         while (tk < nun && tiled_launch_lds(1, F, N, K, tk, d.rows_cap, d.ks, 0).total > kLdsBig) ++tk;
         d.kg = tk;
-    } else if (dense && rows_total >= 2) {
+    } else if (dense && (rows_total >= 2 || tail_sums)) {
+        // (one token: only when the tail sums fp32 partials anyway, as RMSNorm
+        // does; otherwise one K range keeps the residual add in the down kernel)
         d.ts = 1;
         d.ks = 4;
         d.gx = (geo.T + d.ks - 1) / d.ks;
@@ -363,9 +365,9 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int r
 }
 
 KConfig down_tiled_config(int fmt, int K, int N, long long items_est, int rows_total, int cus, bool dense,
-                          int rows_item)
+                          int rows_item, bool tail_sums)
 {
-    const DSplit d = down_tiled_split(fmt, K, N, rows_total, dense, rows_item);
+    const DSplit d = down_tiled_split(fmt, K, N, rows_total, dense, rows_item, tail_sums);
     const int F = to_fmt(fmt);
     const TileGeo geo = tile_geo(F, N, K);
     KConfig c{};
@@ -422,9 +424,9 @@ bool launch_down_tiled(int fmt, const KConfig& c, hipStream_t stream, const Down
 }
 
 // K ranges of the down projection for a format (row-major or tiled).
-int down_ranges(int fmt, int K, int N, int rows_total, bool dense, int rows_item)
+int down_ranges(int fmt, int K, int N, int rows_total, bool dense, int rows_item, bool tail_sums)
 {
-    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total, dense, rows_item).kg
+    return is_tiled(fmt) ? down_tiled_split(fmt, K, N, rows_total, dense, rows_item, tail_sums).kg
                          : down_kg(fmt, K, N, rows_total);
 }
 
@@ -435,11 +437,11 @@ struct DenseWs {
     size_t act, part, logit, total;
 };
 
-DenseWs dense_ws(int fmt_down, int hidden, int inter, int m)
+DenseWs dense_ws(int fmt_down, int hidden, int inter, int m, int tail)
 {
     DenseWs w{};
     size_t o = 0;
-    const int kg = down_ranges(fmt_down, inter, hidden, m, true, m);
+    const int kg = down_ranges(fmt_down, inter, hidden, m, true, m, tail == TAIL_RMSNORM);
     w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * m * hidden * sizeof(float), 256);
     w.logit = o; o += align_up((size_t)m * sizeof(float), 256);
@@ -452,7 +454,7 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
 {
     const int cus = device_cus();
     unsigned char* base = static_cast<unsigned char*>(ws);
-    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m);
+    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail);
     const int gfmt = to_fmt(ffn->gate.fmt), dfmt = to_fmt(ffn->down.fmt);
 
     const bool tiled = is_tiled(ffn->gate.fmt);
@@ -485,7 +487,7 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
         return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true, m)
+    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true, m, tail == TAIL_RMSNORM)
                              : down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
     DownParams dp{};
     dp.down = mat_dev(ffn->down);
@@ -552,7 +554,7 @@ int dense_common(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int
         if (!aux || misaligned(aux)) return FFNQ_ERR_INVALID;
     }
     if (tail == FFNQ_TAIL_RMSNORM && !(eps >= 0.0f && std::isfinite(eps))) return FFNQ_ERR_INVALID;
-    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m);
+    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail);
     if (!ws) {
         *ws_bytes = L.total;
         return FFNQ_OK;
@@ -574,7 +576,7 @@ RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k, int n_exper
 {
     RoutedWs w{};
     const size_t P = (size_t)m * k;
-    const int kg = down_ranges(fmt, moe_inter, hidden, m, false, rows_per_item(false, m, k, n_experts));
+    const int kg = down_ranges(fmt, moe_inter, hidden, m, false, rows_per_item(false, m, k, n_experts), false);
     size_t o = 0;
     w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
@@ -745,7 +747,7 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
 
     // phase 2: down per union entry and tile, d_p to pair_out
     const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false,
-                                                 rows_per_item(false, m, top_k, n_experts))
+                                                 rows_per_item(false, m, top_k, n_experts), false)
                              : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
     DownParams dp{};
     dp.down = mat_dev(experts->down);

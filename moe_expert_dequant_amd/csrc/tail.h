@@ -27,17 +27,22 @@ __device__ __forceinline__ float sum_parts(const float* part, int R, size_t stri
     return h;
 }
 
-// sum_parts for 1 <= R <= 8: one batch, no loop, so that a caller's unrolled
+// sum_parts for 1 <= R <= NB: one batch, no loop, so that a caller's unrolled
 // loop over elements can put several elements' loads in flight together.
-__device__ __forceinline__ float sum_parts8(const float* part, int R, size_t stride, size_t idx)
+template <int NB>
+__device__ __forceinline__ float sum_parts_n(const float* part, int R, size_t stride, size_t idx)
 {
-    float v[8];
+    float v[NB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = part[(size_t)min(j, R - 1) * stride + idx];
+    for (int j = 0; j < NB; ++j) v[j] = part[(size_t)min(j, R - 1) * stride + idx];
     float h = v[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) h = j < R ? h + v[j] : h;
+    for (int j = 1; j < NB; ++j) h = j < R ? h + v[j] : h;
     return h;
+}
+__device__ __forceinline__ float sum_parts8(const float* part, int R, size_t stride, size_t idx)
+{
+    return sum_parts_n<8>(part, R, stride, idx);
 }
 
 // RMSNorm with a bf16 weight over rows of h:
@@ -61,16 +66,16 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
     const size_t stride = (size_t)m * n;
     const bool held = n <= kRowLds;
     double ss = 0.0;
-    if (held && R <= 8) {
-        // four elements per step, their loads together (indices clamped into
-        // the row; only elements < n are kept), added to ss in element order
+    // four elements per step, their loads together (indices clamped into the
+    // row; only elements < n are kept), added to ss in element order
+    auto first_pass = [&](auto sumf) {
         for (int i0 = tid; i0 < n; i0 += 4 * 256) {
             float h4[4];
             uint16_t w4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int ic = min(i0 + 256 * u, n - 1);
-                h4[u] = sum_parts8(part, R, stride, (size_t)t * n + ic);
+                h4[u] = sumf((size_t)t * n + ic);
                 w4[u] = w[ic];
             }
 #pragma unroll
@@ -83,6 +88,11 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
                 }
             }
         }
+    };
+    if (held && R <= 8) {
+        first_pass([&](size_t ix) { return sum_parts_n<8>(part, R, stride, ix); });
+    } else if (held && R <= 16) {
+        first_pass([&](size_t ix) { return sum_parts_n<16>(part, R, stride, ix); });
     } else if (held) {
         for (int i = tid; i < n; i += blockDim.x) {
             const float h = sum_parts(part, R, stride, (size_t)t * n + i);
