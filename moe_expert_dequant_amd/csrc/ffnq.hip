@@ -349,9 +349,10 @@ DSplit down_tiled_split(int fmt, int K, int N, int rows_total, bool dense, int r
         int tk = 1;
         while (tk < nun && tiled_launch_lds(1, F, N, K, tk, d.rows_cap, d.ks, 0).total > kLdsBig) ++tk;
         d.kg = tk;
-    } else if (dense && (rows_total >= 2 || tail_sums)) {
-        // (one token: only when the tail sums fp32 partials anyway, as RMSNorm
-        // does; otherwise one K range keeps the residual add in the down kernel)
+    } else if (dense && (rows_total >= 2 || tail_sums || d.kg > 1)) {
+        // (one token: only when fp32 partials are summed anyway -- by the RMSNorm
+        // tail, or because the K split above already cuts K -- otherwise one K
+        // range keeps the residual add in the down kernel)
         d.ts = 1;
         d.ks = 4;
         d.gx = (geo.T + d.ks - 1) / d.ks;
