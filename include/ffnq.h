@@ -261,6 +261,31 @@ FFNQ_API int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int
                             const uint16_t* seed, uint16_t* resid,
                             void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/* ---- ffnq_moe_layer --------------------------------------------------------
+ * The whole MoE layer after routing in one call ([qwen/moe_batch.rs]
+ * `encode_qwen_layer_moe_batched`: the sigmoid-gated shared expert seeds the
+ * phase-2 accumulator, then the routed half and the raw residual add).  The
+ * result is bit for bit that of
+ *     ffnq_shared_expert(shared, hidden, shared_inter, m, act,
+ *                        FFNQ_TAIL_SIGMOID_GATE, x, seed, shared_gate, ...)
+ *     ffnq_moe_routed_batched(experts, ..., seed, resid, ...)
+ * with seed an internal bf16 [m][hidden] (shared == NULL: no seed).  Fewer
+ * launches: when both are tiled INT4 with matching launch shapes the shared
+ * and routed gate/up run in one launch, and the routed reduction makes the
+ * seed from the shared expert's fp32 partials instead of a separate tail.
+ * experts, topk_ids, topk_w, plan, x, resid: as for ffnq_moe_routed_batched.
+ * shared:       the shared expert's gate/up [shared_inter][hidden] and down
+ *               [hidden][shared_inter] (any supported format), or NULL.
+ * shared_gate:  device bf16 [hidden], the sigmoid gate vector (required with
+ *               shared).
+ * Errors and the workspace contract are those of the two calls it replaces.
+ */
+FFNQ_API int ffnq_moe_layer(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
+                            int act, const ffnq_ffn* shared, int shared_inter, const uint16_t* shared_gate,
+                            const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                            const int32_t* plan, uint16_t* resid, void* ws, size_t* ws_bytes,
+                            hipStream_t stream);
+
 /* ---- ffnq_packed_bytes / ffnq_pack -----------------------------------------
  * Bytes of one n x k matrix (one expert) in a tiled format; fmt may name the
  * row-major format or its tiled form.  0 for an unknown format or shape.

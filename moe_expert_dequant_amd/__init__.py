@@ -29,8 +29,8 @@ TAIL_SIGMOID_GATE = 3
 
 OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
-EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_status_string",
-           "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
+EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_moe_layer",
+           "ffnq_status_string", "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
 
 
 def plan_ints(m: int, k: int) -> int:
@@ -69,7 +69,8 @@ def lib():
         L.ffnq_shared_expert.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
         L.ffnq_moe_route.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
         L.ffnq_moe_routed_batched.argtypes = [FP, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched"):
+        L.ffnq_moe_layer.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for f in ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_moe_layer"):
             getattr(L, f).restype = C.c_int
         L.ffnq_status_string.argtypes = [C.c_int]
         L.ffnq_status_string.restype = C.c_char_p
@@ -200,10 +201,23 @@ def moe_routed_batched(experts: Ffn, n_experts: int, hidden: int, moe_inter: int
     _check("ffnq_moe_routed_batched", L.ffnq_moe_routed_batched(*args, _ptr(buf), C.byref(n), _stream(stream)))
 
 
+def moe_layer(experts: Ffn, n_experts: int, hidden: int, moe_inter: int, m: int, top_k: int, act: int,
+              shared: Ffn | None, shared_inter: int, shared_gate, x, topk_ids, topk_w, plan, resid,
+              ws: Workspace | None = None, stream=None):
+    """ffnq_moe_layer: the gated shared expert (or none) and the routed half in one call."""
+    L = lib()
+    args = (C.byref(experts), n_experts, hidden, moe_inter, m, top_k, act,
+            None if shared is None else C.byref(shared), shared_inter, _ptr(shared_gate), _ptr(x), _ptr(topk_ids),
+            _ptr(topk_w), _ptr(plan), _ptr(resid))
+    buf, n = _ws(L.ffnq_moe_layer, args, ws)
+    _check("ffnq_moe_layer", L.ffnq_moe_layer(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
 def workspace_bytes(kind: str, *args) -> int:
     """Workspace query (ws == NULL) for 'dense', 'shared' or 'routed' with the call's leading arguments."""
     L = lib()
-    fn = {"dense": L.ffnq_dense, "shared": L.ffnq_shared_expert, "routed": L.ffnq_moe_routed_batched}[kind]
+    fn = {"dense": L.ffnq_dense, "shared": L.ffnq_shared_expert, "routed": L.ffnq_moe_routed_batched,
+          "layer": L.ffnq_moe_layer}[kind]
     size = C.c_size_t(0)
     _check(fn.__name__, fn(*args, None, C.byref(size), None))
     return size.value

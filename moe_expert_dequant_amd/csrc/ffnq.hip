@@ -450,6 +450,72 @@ DenseWs dense_ws(int fmt_down, int hidden, int inter, int m, int tail)
     return w;
 }
 
+// Gate/up parameters and configuration of a dense FFN (all m rows, one item).
+// gate_vec/logit: the sigmoid-gate logits, computed by the same launch.
+GUParams dense_gu_params(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, const uint16_t* x,
+                         const KConfig& gc, uint16_t* act_out, const uint16_t* gate_vec, float* logit)
+{
+    GUParams gp{};
+    gp.gate = mat_dev(ffn->gate);
+    gp.up = mat_dev(ffn->up);
+    gp.N = inter;
+    gp.K = hidden;
+    gp.act = act;
+    gp.dfmt = to_fmt(ffn->down.fmt);
+    gp.x = x;
+    gp.m = m;
+    gp.rows_cap = gc.rows_cap;
+    gp.plan = nullptr;
+    gp.act_out = act_out;
+    gp.act_rows = m;
+    gp.gate_vec = gate_vec;
+    gp.logit = logit;
+    if (is_tiled(ffn->gate.fmt)) {
+        gp.tgate = static_cast<const uint8_t*>(ffn->gate.q);
+        gp.tup = static_cast<const uint8_t*>(ffn->up.q);
+        gp.tebytes = tiled_expert_bytes(ffn->gate);
+        gp.dfmt = FMT_NATURAL;   // a tiled down matrix reads the activation in natural order
+    }
+    return gp;
+}
+
+KConfig dense_gu_config(const ffnq_ffn* ffn, int hidden, int inter, int m, int cus)
+{
+    return is_tiled(ffn->gate.fmt) ? gu_tiled_config(ffn->gate.fmt, hidden, inter, 1, m, cus, m)
+                                   : gu_config(ffn->gate.fmt, hidden, inter, 1, m, cus);
+}
+
+KConfig dense_down_config(const ffnq_ffn* ffn, int hidden, int inter, int m, int cus, int tail)
+{
+    return is_tiled(ffn->down.fmt)
+               ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true, m, tail == FFNQ_TAIL_RMSNORM)
+               : down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
+}
+
+DownParams dense_down_params(const ffnq_ffn* ffn, int hidden, int inter, int m, const KConfig& dc,
+                             const uint16_t* act, uint16_t* out, float* part, const float* logit, int dtail)
+{
+    DownParams dp{};
+    dp.down = mat_dev(ffn->down);
+    dp.N = hidden;
+    dp.K = inter;
+    dp.act = act;
+    dp.act_rows = m;
+    dp.m = m;
+    dp.rows_cap = dc.rows_cap;
+    dp.KG = dc.kg;
+    dp.plan = nullptr;
+    dp.out = out;
+    dp.part = part;
+    dp.logit = logit;
+    dp.tail = dtail;
+    if (is_tiled(ffn->down.fmt)) {
+        dp.tdown = static_cast<const uint8_t*>(ffn->down.q);
+        dp.tebytes = tiled_expert_bytes(ffn->down);
+    }
+    return dp;
+}
+
 int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail, const uint16_t* x,
               uint16_t* out, const uint16_t* aux, float eps, void* ws, hipStream_t stream)
 {
@@ -457,62 +523,27 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
     unsigned char* base = static_cast<unsigned char*>(ws);
     const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail);
     const int gfmt = to_fmt(ffn->gate.fmt), dfmt = to_fmt(ffn->down.fmt);
-
     const bool tiled = is_tiled(ffn->gate.fmt);
-    const KConfig gc = tiled ? gu_tiled_config(ffn->gate.fmt, hidden, inter, 1, m, cus, m)
-                             : gu_config(ffn->gate.fmt, hidden, inter, 1, m, cus);
-    GUParams gp{};
-    gp.gate = mat_dev(ffn->gate);
-    gp.up = mat_dev(ffn->up);
-    gp.N = inter;
-    gp.K = hidden;
-    gp.act = act;
-    gp.dfmt = dfmt;
-    gp.x = x;
-    gp.m = m;
-    gp.rows_cap = gc.rows_cap;
-    gp.plan = nullptr;
-    gp.act_out = reinterpret_cast<uint16_t*>(base + L.act);
-    gp.act_rows = m;
-    if (tail == FFNQ_TAIL_SIGMOID_GATE) {
-        gp.gate_vec = aux;
-        gp.logit = reinterpret_cast<float*>(base + L.logit);
-    }
-    if (tiled) {
-        gp.tgate = static_cast<const uint8_t*>(ffn->gate.q);
-        gp.tup = static_cast<const uint8_t*>(ffn->up.q);
-        gp.tebytes = tiled_expert_bytes(ffn->gate);
-        gp.dfmt = FMT_NATURAL;   // a tiled down matrix reads the activation in natural order
-    }
+
+    const KConfig gc = dense_gu_config(ffn, hidden, inter, m, cus);
+    const bool sg = tail == FFNQ_TAIL_SIGMOID_GATE;
+    const GUParams gp = dense_gu_params(ffn, hidden, inter, m, act, x, gc, reinterpret_cast<uint16_t*>(base + L.act),
+                                        sg ? aux : nullptr, sg ? reinterpret_cast<float*>(base + L.logit) : nullptr);
     if (!(tiled ? launch_gu_tiled(gfmt, gc, stream, gp) : launch_gu(gfmt, gc, 1, inter, stream, gp)))
         return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    const KConfig dc = tiled ? down_tiled_config(ffn->down.fmt, inter, hidden, 1, m, cus, true, m, tail == TAIL_RMSNORM)
-                             : down_config(ffn->down.fmt, inter, hidden, 1, m, cus);
-    DownParams dp{};
-    dp.down = mat_dev(ffn->down);
-    dp.N = hidden;
-    dp.K = inter;
-    dp.act = gp.act_out;
-    dp.act_rows = m;
-    dp.m = m;
-    dp.rows_cap = dc.rows_cap;
-    dp.KG = dc.kg;
-    dp.plan = nullptr;
-    dp.out = out;
-    dp.part = reinterpret_cast<float*>(base + L.part);
-    dp.logit = reinterpret_cast<const float*>(base + L.logit);
+    const KConfig dc = dense_down_config(ffn, hidden, inter, m, cus, tail);
+    int dtail = TAIL_NONE;
     switch (tail) {
-        case FFNQ_TAIL_RESIDUAL: dp.tail = TAIL_RESIDUAL; break;
-        case FFNQ_TAIL_RMSNORM: dp.tail = TAIL_RMSNORM; break;
-        case FFNQ_TAIL_SIGMOID_GATE: dp.tail = TAIL_SIGMOID; break;
-        default: dp.tail = TAIL_NONE; break;
+        case FFNQ_TAIL_RESIDUAL: dtail = TAIL_RESIDUAL; break;
+        case FFNQ_TAIL_RMSNORM: dtail = TAIL_RMSNORM; break;
+        case FFNQ_TAIL_SIGMOID_GATE: dtail = TAIL_SIGMOID; break;
+        default: break;
     }
-    if (tiled) {
-        dp.tdown = static_cast<const uint8_t*>(ffn->down.q);
-        dp.tebytes = tiled_expert_bytes(ffn->down);
-    }
+    const DownParams dp = dense_down_params(ffn, hidden, inter, m, dc, gp.act_out, out,
+                                            reinterpret_cast<float*>(base + L.part),
+                                            reinterpret_cast<const float*>(base + L.logit), dtail);
     if (!(tiled ? launch_down_tiled(dfmt, dc, stream, dp) : launch_down(dfmt, dc, 1, hidden, stream, dp)))
         return FFNQ_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
@@ -583,6 +614,154 @@ RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k, int n_exper
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
     w.total = m == 0 ? 0 : o;
     return w;
+}
+
+// The shared expert of a MoE layer when it runs fused with the routed half
+// (ffnq_moe_layer): its gate/up shares the routed gate/up launch when their
+// launch shapes agree, its down leaves fp32 partials, and the routed reduction
+// makes the seed from them.  Same arithmetic as ffnq_shared_expert followed by
+// ffnq_moe_routed_batched.
+struct LayerShared {
+    const ffnq_ffn* ffn;
+    int inter;
+    const uint16_t* gate_vec;
+    unsigned char* base;   // its workspace (dense_ws with the sigmoid-gate tail)
+};
+
+#define FFNQ_GUT2_CASE(NT_, MT_)                                                                       \
+    if (a.nt == NT_ && a.mt == MT_) {                                                                  \
+        hipExtLaunchKernelGGL((gu_tiled_kernel2<FMT_INT4, NT_, MT_>), grid, dim3(64 * a.ks), lds, stream, \
+                              phase_event(0), phase_event(1), 0, qa, qb);                              \
+        return true;                                                                                   \
+    }
+
+// Shared and routed tiled INT4 gate/up in one launch (grid rows 0 and 1).
+bool launch_gu_tiled2(const KConfig& a, const GUParams& pa, const KConfig& b, const GUParams& pb, hipStream_t stream)
+{
+    if (a.nt != b.nt || a.mt != b.mt || a.ks != b.ks || a.ts || b.ts) return false;
+    GUParams qa = pa, qb = pb;
+    qa.ks = a.ks;
+    qa.grid = a.grid;
+    qb.ks = b.ks;
+    qb.grid = b.grid;
+    const dim3 grid((unsigned)std::max(a.grid, b.grid), 2);
+    const size_t lds = std::max(a.lds, b.lds);
+    FFNQ_GUT2_CASE(1, 1) FFNQ_GUT2_CASE(1, 2) FFNQ_GUT2_CASE(1, 4) FFNQ_GUT2_CASE(2, 4)
+    return false;
+}
+
+// The routed half on a checked call (m > 0; the routed workspace at base).
+int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
+               const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
+               const uint16_t* seed, uint16_t* resid, unsigned char* base, hipStream_t stream, const LayerShared* sh)
+{
+    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
+    const int cus = device_cus();
+    const int P = m * top_k;
+    const long long u_est = std::min<long long>(P, n_experts);
+
+    // phase 1: gate/up + activation per union entry and tile
+    const bool tiled = is_tiled(experts->gate.fmt);
+    const KConfig gc = tiled ? gu_tiled_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus,
+                                               rows_per_item(false, m, top_k, n_experts))
+                             : gu_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus);
+    GUParams gp{};
+    gp.gate = mat_dev(experts->gate);
+    gp.up = mat_dev(experts->up);
+    gp.N = moe_inter;
+    gp.K = hidden;
+    gp.act = act;
+    gp.dfmt = FMT_INT4;
+    gp.x = x;
+    gp.m = m;
+    gp.rows_cap = gc.rows_cap;
+    gp.plan = plan;
+    gp.top_k = top_k;
+    gp.topk_ids = topk_ids;
+    gp.n_experts = n_experts;
+    gp.act_out = reinterpret_cast<uint16_t*>(base + L.act);
+    gp.act_rows = P;
+    if (tiled) {
+        gp.tgate = static_cast<const uint8_t*>(experts->gate.q);
+        gp.tup = static_cast<const uint8_t*>(experts->up.q);
+        gp.tebytes = tiled_expert_bytes(experts->gate);
+        gp.dfmt = FMT_NATURAL;
+    }
+    KConfig gcs{};
+    GUParams gps{};
+    DenseWs Ls{};
+    if (sh) {
+        Ls = dense_ws(sh->ffn->down.fmt, hidden, sh->inter, m, FFNQ_TAIL_SIGMOID_GATE);
+        gcs = dense_gu_config(sh->ffn, hidden, sh->inter, m, cus);
+        gps = dense_gu_params(sh->ffn, hidden, sh->inter, m, act, x, gcs,
+                              reinterpret_cast<uint16_t*>(sh->base + Ls.act), sh->gate_vec,
+                              reinterpret_cast<float*>(sh->base + Ls.logit));
+    }
+    if (sh && tiled && is_tiled(sh->ffn->gate.fmt) && is_int4(sh->ffn->gate.fmt) &&
+        launch_gu_tiled2(gcs, gps, gc, gp, stream)) {
+        // shared and routed gate/up in one launch
+    } else {
+        if (sh) {
+            const int sfmt = to_fmt(sh->ffn->gate.fmt);
+            if (!(is_tiled(sh->ffn->gate.fmt) ? launch_gu_tiled(sfmt, gcs, stream, gps)
+                                              : launch_gu(sfmt, gcs, 1, sh->inter, stream, gps)))
+                return FFNQ_ERR_UNSUPPORTED;
+        }
+        if (!(tiled ? launch_gu_tiled(FMT_INT4, gc, stream, gp) : launch_gu(FMT_INT4, gc, u_est, moe_inter, stream, gp)))
+            return FFNQ_ERR_UNSUPPORTED;
+    }
+    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+
+    // the shared expert's down: fp32 K-range partials, the seed is made by the reduction
+    KConfig dcs{};
+    DownParams dps{};
+    if (sh) {
+        dcs = dense_down_config(sh->ffn, hidden, sh->inter, m, cus, FFNQ_TAIL_SIGMOID_GATE);
+        dps = dense_down_params(sh->ffn, hidden, sh->inter, m, dcs, gps.act_out, nullptr,
+                                reinterpret_cast<float*>(sh->base + Ls.part),
+                                reinterpret_cast<const float*>(sh->base + Ls.logit), TAIL_PART);
+        const int sdfmt = to_fmt(sh->ffn->down.fmt);
+        if (!(is_tiled(sh->ffn->down.fmt) ? launch_down_tiled(sdfmt, dcs, stream, dps)
+                                          : launch_down(sdfmt, dcs, 1, hidden, stream, dps)))
+            return FFNQ_ERR_UNSUPPORTED;
+        if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    }
+
+    // phase 2: down per union entry and tile, d_p to pair_out
+    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false,
+                                                 rows_per_item(false, m, top_k, n_experts), false)
+                             : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
+    DownParams dp{};
+    dp.down = mat_dev(experts->down);
+    dp.N = hidden;
+    dp.K = moe_inter;
+    dp.act = gp.act_out;
+    dp.act_rows = P;
+    dp.m = m;
+    dp.rows_cap = dc.rows_cap;
+    dp.KG = dc.kg;
+    dp.plan = plan;
+    dp.top_k = top_k;
+    dp.topk_ids = topk_ids;
+    dp.n_experts = n_experts;
+    dp.tail = TAIL_PAIR;
+    dp.part = reinterpret_cast<float*>(base + L.part);
+    if (tiled) {
+        dp.tdown = static_cast<const uint8_t*>(experts->down.q);
+        dp.tebytes = tiled_expert_bytes(experts->down);
+    }
+    if (!(tiled ? launch_down_tiled(FMT_INT4, dc, stream, dp) : launch_down(FMT_INT4, dc, u_est, hidden, stream, dp)))
+        return FFNQ_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+
+    // seeded rank-ordered reduce + residual
+    const long long total = (long long)m * hidden;
+    const int rgrid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
+    hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, dc.kg, topk_w, topk_ids,
+                       n_experts, sh ? nullptr : seed, resid, m, top_k, hidden, sh ? dps.part : nullptr,
+                       sh ? dcs.kg : 0, sh ? dps.logit : nullptr);
+    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    return FFNQ_OK;
 }
 
 }  // namespace
@@ -710,76 +889,50 @@ int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, 
     if (misaligned(ws)) return FFNQ_ERR_INVALID;
     if (m == 0) return FFNQ_OK;
 
-    const int cus = device_cus();
+    return run_routed(experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan, seed, resid,
+                      static_cast<unsigned char*>(ws), stream, nullptr);
+}
+
+int ffnq_moe_layer(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
+                   const ffnq_ffn* shared, int shared_inter, const uint16_t* shared_gate, const uint16_t* x,
+                   const int32_t* topk_ids, const float* topk_w, const int32_t* plan, uint16_t* resid, void* ws,
+                   size_t* ws_bytes, hipStream_t stream)
+{
+    if (!ws_bytes) return FFNQ_ERR_INVALID;
+    if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
+    int rc = check_ffn(experts, hidden, moe_inter);
+    if (rc != FFNQ_OK) return rc;
+    if (!is_int4(experts->gate.fmt) || !is_int4(experts->up.fmt) || !is_int4(experts->down.fmt))
+        return FFNQ_ERR_UNSUPPORTED;
+    if (shared) {
+        rc = check_ffn(shared, hidden, shared_inter);
+        if (rc != FFNQ_OK) return rc;
+        if (!shared_gate || misaligned(shared_gate)) return FFNQ_ERR_INVALID;
+    }
+    if (act != FFNQ_ACT_SILU && act != FFNQ_ACT_GELU_TANH) return FFNQ_ERR_UNSUPPORTED;
+    if (!x || !topk_ids || !topk_w || !plan || !resid) return FFNQ_ERR_INVALID;
+    if (misaligned(x) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(plan) || misaligned(resid))
+        return FFNQ_ERR_INVALID;
+    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
+    const size_t rows_bytes = (size_t)m * hidden * 2;
+    if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
+    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
+    const size_t shared_off = align_up(L.total, 256);
+    const size_t total = m == 0 ? 0
+                                : shared_off + (shared ? dense_ws(shared->down.fmt, hidden, shared_inter, m,
+                                                                  FFNQ_TAIL_SIGMOID_GATE).total
+                                                       : 0);
+    if (!ws) {
+        *ws_bytes = total;
+        return FFNQ_OK;
+    }
+    if (*ws_bytes < total) return FFNQ_ERR_WORKSPACE;
+    if (misaligned(ws)) return FFNQ_ERR_INVALID;
+    if (m == 0) return FFNQ_OK;
     unsigned char* base = static_cast<unsigned char*>(ws);
-    const int P = m * top_k;
-    const long long u_est = std::min<long long>(P, n_experts);
-
-    // phase 1: gate/up + activation per union entry and tile
-    const bool tiled = is_tiled(experts->gate.fmt);
-    const KConfig gc = tiled ? gu_tiled_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus,
-                                               rows_per_item(false, m, top_k, n_experts))
-                             : gu_config(experts->gate.fmt, hidden, moe_inter, u_est, m, cus);
-    GUParams gp{};
-    gp.gate = mat_dev(experts->gate);
-    gp.up = mat_dev(experts->up);
-    gp.N = moe_inter;
-    gp.K = hidden;
-    gp.act = act;
-    gp.dfmt = FMT_INT4;
-    gp.x = x;
-    gp.m = m;
-    gp.rows_cap = gc.rows_cap;
-    gp.plan = plan;
-    gp.top_k = top_k;
-    gp.topk_ids = topk_ids;
-    gp.n_experts = n_experts;
-    gp.act_out = reinterpret_cast<uint16_t*>(base + L.act);
-    gp.act_rows = P;
-    if (tiled) {
-        gp.tgate = static_cast<const uint8_t*>(experts->gate.q);
-        gp.tup = static_cast<const uint8_t*>(experts->up.q);
-        gp.tebytes = tiled_expert_bytes(experts->gate);
-        gp.dfmt = FMT_NATURAL;
-    }
-    if (!(tiled ? launch_gu_tiled(FMT_INT4, gc, stream, gp) : launch_gu(FMT_INT4, gc, u_est, moe_inter, stream, gp)))
-        return FFNQ_ERR_UNSUPPORTED;
-    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
-
-    // phase 2: down per union entry and tile, d_p to pair_out
-    const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false,
-                                                 rows_per_item(false, m, top_k, n_experts), false)
-                             : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
-    DownParams dp{};
-    dp.down = mat_dev(experts->down);
-    dp.N = hidden;
-    dp.K = moe_inter;
-    dp.act = gp.act_out;
-    dp.act_rows = P;
-    dp.m = m;
-    dp.rows_cap = dc.rows_cap;
-    dp.KG = dc.kg;
-    dp.plan = plan;
-    dp.top_k = top_k;
-    dp.topk_ids = topk_ids;
-    dp.n_experts = n_experts;
-    dp.tail = TAIL_PAIR;
-    dp.part = reinterpret_cast<float*>(base + L.part);
-    if (tiled) {
-        dp.tdown = static_cast<const uint8_t*>(experts->down.q);
-        dp.tebytes = tiled_expert_bytes(experts->down);
-    }
-    if (!(tiled ? launch_down_tiled(FMT_INT4, dc, stream, dp) : launch_down(FMT_INT4, dc, u_est, hidden, stream, dp)))
-        return FFNQ_ERR_UNSUPPORTED;
-    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
-
-    // seeded rank-ordered reduce + residual
-    const long long total = (long long)m * hidden;
-    const int rgrid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
-    hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, dc.kg, topk_w, topk_ids,
-                       n_experts, seed, resid, m, top_k, hidden);
-    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
-    return FFNQ_OK;
+    const LayerShared lsh{shared, shared_inter, shared_gate, base + shared_off};
+    return run_routed(experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan, nullptr, resid,
+                      base, stream, shared ? &lsh : nullptr);
 }
 
 }  // extern "C"

@@ -610,7 +610,8 @@ __global__ void __launch_bounds__(512) gu_kernel(GUParams p)
 // here; otherwise (and for the RMSNORM and routed tails) the workgroup writes
 // its fp32 partial h to part[range][row][n] for the kernel that follows.
 
-enum { TAIL_NONE = 0, TAIL_RESIDUAL = 1, TAIL_RMSNORM = 2, TAIL_SIGMOID = 3, TAIL_PAIR = 4 };
+enum { TAIL_NONE = 0, TAIL_RESIDUAL = 1, TAIL_RMSNORM = 2, TAIL_SIGMOID = 3, TAIL_PAIR = 4,
+       TAIL_PART = 5 };   // TAIL_PART: fp32 partials only, for a later kernel to finish
 
 struct DownParams {
     MatDev down;
@@ -635,7 +636,7 @@ struct DownParams {
 
 __device__ __forceinline__ void down_finish(const DownParams& p, int t, int n, float h)
 {
-    if (p.KG > 1 || p.tail == TAIL_PAIR || p.tail == TAIL_RMSNORM) {
+    if (p.KG > 1 || p.tail == TAIL_PAIR || p.tail == TAIL_RMSNORM || p.tail == TAIL_PART) {
         const size_t rows = p.tail == TAIL_PAIR ? (size_t)p.act_rows : (size_t)p.m;
         p.part[((size_t)blockIdx.y * rows + t) * p.N + n] = h;
     } else if (p.tail == TAIL_RESIDUAL) {

@@ -170,17 +170,28 @@ __device__ __forceinline__ float moe_ranks(const float* __restrict__ part, int R
 // tail is one residual add, no norm).  d = down_e(act_p) per pair p comes from
 // the grouped down kernel.  Product and sum are each rounded to fp32
 // (no fused multiply-add), in rank order.
+// The seed is either a bf16 row (seed) or made here from the shared expert's
+// fp32 K-range partials (shpart, shR ranges) and its gate logits: the same
+// bf16(h * sigmoid(logit)) in double that the shared expert's own tail writes.
 __global__ void __launch_bounds__(256) moe_reduce_kernel(const float* __restrict__ part, int R,
                                                          const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ topk_ids, int n_experts,
                                                          const uint16_t* __restrict__ seed, uint16_t* __restrict__ resid,
-                                                         int m, int k, int n)
+                                                         int m, int k, int n, const float* __restrict__ shpart,
+                                                         int shR, const float* __restrict__ logit)
 {
     const size_t total = (size_t)m * n;
     const size_t stride = (size_t)m * k * n;
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
         const int t = (int)(idx / n), i = (int)(idx - (size_t)t * n);
-        float acc = seed ? bf16_f32(seed[idx]) : 0.0f;
+        float acc = 0.0f;
+        if (shpart) {
+            const double h = (double)sum_parts(shpart, shR, total, idx);
+            const double sg = 1.0 / (1.0 + exp(-(double)logit[t]));
+            acc = bf16_f32(bf16_from_f64(h * sg));
+        } else if (seed) {
+            acc = bf16_f32(seed[idx]);
+        }
         const float rs = bf16_f32(resid[idx]);
         if (k <= 2)
             acc = moe_ranks<2>(part, R, stride, topk_w, topk_ids, n_experts, t, k, n, i, acc);

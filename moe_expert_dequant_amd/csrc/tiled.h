@@ -557,7 +557,8 @@ struct TiledJob {
     int m, act_rows;
     const int32_t* topk_ids;
     int n_experts;
-    int KS, G;                // waves per workgroup, gridDim.x
+    int KS, G;                // waves per workgroup, workgroups along x
+    int bx, by;               // this workgroup (the kernel may run several jobs side by side)
 };
 
 template <int FMT, int NMAT, int NT, int MT, bool HILO, bool TS, typename Rows, typename Finish>
@@ -573,7 +574,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
     const int T = geo.T;
     const int nun = FMT == FMT_INT4 ? geo.ng : geo.nbk;   // K units: groups or blocks
     // K range of this grid row and of this wave (32-bit: nun * KG is small)
-    const int U0 = nun * (int)blockIdx.y / J.KG, U1 = nun * ((int)blockIdx.y + 1) / J.KG;
+    const int U0 = nun * J.by / J.KG, U1 = nun * (J.by + 1) / J.KG;
     const int kb0 = FMT == FMT_INT4 ? 8 * U0 : U0;
     const int kb1 = FMT == FMT_INT4 ? min(8 * U1, geo.nbk) : U1;
     const int u0w = TS ? U0 : U0 + (U1 - U0) * w / KS, u1w = TS ? U1 : U0 + (U1 - U0) * (w + 1) / KS;
@@ -583,7 +584,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
     const int n_units = (J.routed ? J.pv.n_union() : 1) * T;
     const int G = J.G;
     const int RL = red_lanes(NT, J.rows_cap);   // lanes kept by the reduction (uniform)
-    for (int u0 = blockIdx.x; u0 < n_units;) {
+    for (int u0 = J.bx; u0 < n_units;) {
         int item = 0, run;
         if (!J.routed) {
             run = (n_units - u0 + G - 1) / G;   // every unit belongs to the one item
@@ -761,7 +762,7 @@ __device__ __forceinline__ void tiled_body(const TiledJob& J, Rows rows, Finish 
 // launch shape comes in the arguments too (ks, grid) rather than from the
 // dispatch packet.
 template <int FMT, int NT, int MT, bool TS>
-__global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
+__device__ __forceinline__ void gu_tiled_run(const GUParams& p, int bx, int by)
 {
     asm volatile("" ::"s"(p.tgate), "s"(p.tup), "s"(p.tebytes), "s"(p.N), "s"(p.K), "s"(p.x), "s"(p.rows_cap),
                  "s"(p.plan), "s"(p.m), "s"(p.top_k), "s"(p.act_rows), "s"(p.topk_ids), "s"(p.n_experts), "s"(p.act),
@@ -786,6 +787,8 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
     J.n_experts = p.n_experts;
     J.KS = p.ks;
     J.G = p.grid;
+    J.bx = bx;
+    J.by = by;
     const int act = p.act, dfmt = p.dfmt;
     uint16_t* const act_out = p.act_out;
     const uint16_t* const gate_vec = p.gate_vec;
@@ -810,7 +813,7 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
     tiled_body<FMT, 2, NT, MT, false, TS>(J, rows, finish);
     // shared-expert gate logits (read by the down kernel's tail): one
     // workgroup, after its tiles
-    if (gate_vec != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+    if (gate_vec != nullptr && bx == 0 && by == 0) {
         const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, nw = J.KS;
         for (int t = w; t < J.m; t += nw) {
             double acc = 0.0;
@@ -820,6 +823,25 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
             if (lane == 0) logit[t] = (float)acc;
         }
     }
+}
+
+template <int FMT, int NT, int MT, bool TS>
+__global__ void __launch_bounds__(512) gu_tiled_kernel(GUParams p)
+{
+    gu_tiled_run<FMT, NT, MT, TS>(p, blockIdx.x, blockIdx.y);
+}
+
+// Two gate/up jobs in one launch (e.g. a layer's shared expert and its routed
+// experts, both reading x): grid row 0 runs job a, row 1 job b, each over its
+// own p.grid workgroups along x.  The jobs share the template shape and the
+// waves per workgroup; each lays out its own LDS within the launch's allocation.
+template <int FMT, int NT, int MT>
+__global__ void __launch_bounds__(512) gu_tiled_kernel2(GUParams a, GUParams b)
+{
+    const bool jb = blockIdx.y != 0;
+    const GUParams& p = jb ? b : a;
+    if ((int)blockIdx.x >= p.grid) return;
+    gu_tiled_run<FMT, NT, MT, false>(p, blockIdx.x, 0);
 }
 
 // down + tail: h per (token or pair, hidden row), finished by down_finish
@@ -849,6 +871,8 @@ __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
     J.n_experts = p.n_experts;
     J.KS = p.ks;
     J.G = p.grid;
+    J.bx = blockIdx.x;
+    J.by = blockIdx.y;
     auto rows = [&](const Item& it, int c0, int t, long long* roff, int* orows) {
         const int xr = c0 + t, li = xr >> 1;
         int arow = li;

@@ -169,6 +169,35 @@ def test_routed_refusals_and_query():
     assert call_routed(f, ws=addr(60), ws_bytes=n - 256)[0] == -4
 
 
+def call_layer(f, sh, E=8, hidden=256, inter=256, sh_inter=512, m=3, k=2, act=fq.ACT_SILU, gate=addr(45), x=addr(40),
+               ids=addr(41), w=addr(42), plan=addr(43), resid=addr(50), ws=None, ws_bytes=0):
+    L = fq.lib()
+    size = C.c_size_t(ws_bytes)
+    rc = L.ffnq_moe_layer(C.byref(f), E, hidden, inter, m, k, act, None if sh is None else C.byref(sh), sh_inter, gate,
+                          x, ids, w, plan, resid, ws, C.byref(size), None)
+    return rc, size.value
+
+
+def test_layer_refusals_and_query():
+    f, sh = ffn(I4, I4, 256, 256), ffn(I4, I4, 256, 512)
+    rc, n = call_layer(f, sh)
+    assert rc == 0
+    rc0, n0 = call_layer(f, None)
+    assert rc0 == 0
+    # the workspace holds the routed half's (as ffnq_moe_routed_batched sizes it) and then the shared expert's
+    assert n0 == call_routed(f)[1]
+    assert n > n0
+    assert call_layer(f, sh, m=0) == (0, 0)
+    assert call_layer(ffn(I8, I4, 256, 256), sh)[0] == -2      # routed experts must be INT4-affine
+    assert call_layer(f, sh, gate=None)[0] == -1               # the shared expert needs its gate vector
+    assert call_layer(f, sh, gate=addr(45) + 2)[0] == -1       # misaligned
+    assert call_layer(f, sh, sh_inter=256)[0] != 0             # shared matrices disagree with shared_inter
+    assert call_layer(f, sh, k=9)[0] == -1
+    assert call_layer(f, sh, act=3)[0] == -2
+    assert call_layer(f, sh, resid=addr(40) + 64)[0] == -1     # overlaps x
+    assert call_layer(f, sh, ws=addr(60), ws_bytes=n - 256)[0] == -4
+
+
 # ---------------------------------------------------------------------------
 # tiled formats and ffnq_pack (refusals only: no launch)
 

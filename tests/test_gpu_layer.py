@@ -1,0 +1,120 @@
+"""ffnq_moe_layer: the gated shared expert and the routed half in one call.
+
+Its contract is the two-call sequence ffnq_shared_expert(SIGMOID_GATE) ->
+seed -> ffnq_moe_routed_batched(seed), bit for bit, whichever launch plan it
+takes (shared and routed gate/up in one launch when both are tiled INT4 with
+matching launch shapes, separate launches otherwise).  The two-call sequence
+is checked against the oracle in test_gpu_parity; here the layer is compared
+with it exactly, and once more with the oracle within the float bar."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import moe_expert_dequant_amd as fq
+import oracle
+from helpers import rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def dev16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def mats(f, tiled, n_experts=1):
+    d = {n: fq.to_device(f[n]) for n in ("gate", "up", "down")}
+    if tiled:
+        d = {n: fq.pack(d[n], n_experts) for n in d}
+    return d, fq.ffn_struct(d)
+
+
+def route(logits, k, cap):
+    m, E = logits.shape
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    fq.moe_route(dev(logits.astype(np.float32)), m, E, k, cap, ids, w, plan)
+    return ids, w, plan
+
+
+def two_calls(ex, sh, E, hidden, inter, sh_inter, m, k, act, x, gate, ids, w, plan, resid0):
+    resid = resid0.clone()
+    seed = None
+    if sh is not None:
+        seed = torch.zeros((m, hidden), dtype=torch.int16, device="cuda")
+        fq.shared_expert(sh, hidden, sh_inter, m, act, gen.TAIL_SIGMOID_GATE, x, seed, gate)
+    fq.moe_routed_batched(ex, E, hidden, inter, m, k, act, x, ids, w, plan, seed, resid)
+    torch.cuda.synchronize()
+    return host16(resid), None if seed is None else host16(seed)
+
+
+def one_call(ex, sh, E, hidden, inter, sh_inter, m, k, act, x, gate, ids, w, plan, resid0):
+    resid = resid0.clone()
+    fq.moe_layer(ex, E, hidden, inter, m, k, act, sh, sh_inter, gate, x, ids, w, plan, resid)
+    torch.cuda.synchronize()
+    return host16(resid)
+
+
+def run_case(inp, E, hidden, inter, sh_inter, m, k, cap, act, tiled_ex, sh_fmt_tiled):
+    ex_d, ex = mats(inp["experts"], tiled_ex, E)
+    sh = None
+    if sh_inter:
+        sh_d, sh = mats(inp["shared"], sh_fmt_tiled)
+    x = dev16(inp["x"])
+    gate = dev16(inp["gate_vec"]) if sh_inter else None
+    resid0 = dev16(inp["resid"])
+    ids, w, plan = route(inp["logits"], k, cap)
+    want, seed = two_calls(ex, sh, E, hidden, inter, sh_inter, m, k, act, x, gate, ids, w, plan, resid0)
+    got = one_call(ex, sh, E, hidden, inter, sh_inter, m, k, act, x, gate, ids, w, plan, resid0)
+    assert np.array_equal(got, want)
+    return got, seed, ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_layer_config3_matches_two_calls(m):
+    c = gen.CONFIGS[3]
+    say("layer config3", m)
+    inp = gen.config_inputs(3, m)
+    hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
+    got, seed, ids, w = run_case(inp, E, hidden, inter, c["shared_inter"], m, k, c["cap"], c["act"], True, True)
+    want = oracle.moe_routed(inp["experts"], E, hidden, inter, c["act"], inp["x"], ids, w, seed, inp["resid"])
+    assert rel_l2_rows(got, want) <= TOL
+
+
+@pytest.mark.parametrize("m,k,cap,tiled_ex,sh_tiled,sh_fmt", [
+    (1, 4, 8, True, True, gen.FMT_INT4_AFFINE_G64),     # one gate/up launch for both
+    (5, 4, 8, True, True, gen.FMT_INT4_AFFINE_G64),     # ragged rows, several sub-batches
+    (3, 2, 8, False, False, gen.FMT_INT4_AFFINE_G64),   # row-major: separate launches
+    (4, 4, 8, True, False, gen.FMT_INT8_ROW),           # INT8 row-major shared expert, tiled experts
+    (20, 2, 16, True, True, gen.FMT_INT4_AFFINE_G64),   # more rows per expert
+])
+def test_layer_small_matches_two_calls(m, k, cap, tiled_ex, sh_tiled, sh_fmt):
+    hidden, inter, E, sh_inter = 512, 256, 16, 384
+    say("layer small", m, k, cap, tiled_ex, sh_tiled, sh_fmt)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4600 + m + 10 * k)
+    inp["shared"] = gen.ffn(sh_fmt, sh_fmt, hidden, sh_inter, gen.tensor_key(4700 + m, 1))
+    inp["gate_vec"] = gen.gate_vector(gen.tensor_key(4701 + m, 2), hidden)
+    run_case(inp, E, hidden, inter, sh_inter, m, k, cap, gen.ACT_SILU, tiled_ex, sh_tiled)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_layer_without_shared_is_unseeded_routed(tiled):
+    hidden, inter, E, m, k, cap = 512, 256, 16, 3, 4, 8
+    say("layer no shared", tiled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4800)
+    run_case(inp, E, hidden, inter, 0, m, k, cap, gen.ACT_SILU, tiled, tiled)
