@@ -257,17 +257,13 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
         exs = [ex] + [_clone_mats(ex) for _ in range(copies - 1)]
         ex_st = [fq.ffn_struct(d) for d in exs]
         shs = None if sh is None else [fq.ffn_struct(d) for d in ([sh] + [_clone_mats(sh) for _ in range(copies - 1)])]
-        seed = torch.zeros((m, hidden), dtype=torch.int16, device="cuda") if sh is not None else None
         gv = _dev16(inp["gate_vec"]) if sh is not None else None
-        ws2 = fq.Workspace()
 
-        def call(i):
-            if shs is not None:
-                fq.shared_expert(shs[i % copies], hidden, cfg["shared_inter"], m, cfg["act"], gen.TAIL_SIGMOID_GATE,
-                                 x, seed, gv, ws=ws2)
+        def call(i):   # router top-k + plan, then the gated shared expert and the routed half in one call
             fq.moe_route(logits, m, E, k, cap, ids, w, plan)
-            fq.moe_routed_batched(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"], x, ids, w, plan, seed, resid,
-                                  ws=ws)
+            fq.moe_layer(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"],
+                         None if shs is None else shs[i % copies], cfg["shared_inter"] or 0, gv, x, ids, w, plan,
+                         resid, ws=ws)
         counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
         extra = dict(union=union, sub_batches=n_sub, tokens_per_expert_min=int(counts[counts > 0].min()),
                      tokens_per_expert_max=int(counts.max()))

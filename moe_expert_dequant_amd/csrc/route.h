@@ -37,6 +37,14 @@ __device__ __forceinline__ uint64_t route_key(float l, int e)
     return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// The logit a key was made from (NaN comes back as -inf and -0 as +0, which is
+// how the weights treat them).
+__device__ __forceinline__ float route_key_logit(uint64_t key)
+{
+    const uint32_t ord = (uint32_t)(key >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
     for (int off = 32; off > 0; off >>= 1) {
@@ -53,6 +61,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     __shared__ int ids_s[kIdsCache];
     __shared__ uint64_t keys_s[256 / 64][kRankMax];   // per wave: the token's keys
     __shared__ int sel_s[256 / 64][kRankMax];         // per wave: expert of each rank < k
+    __shared__ float sell_s[256 / 64][kRankMax];      // per wave: logit of each rank < k
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
     const int m = p.m, k = p.k, E = p.E;
     const int nj = (E + 63) >> 6;
@@ -69,6 +78,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
             key[j] = (j < nj && e < E) ? route_key(p.logits[(size_t)t * E + e], e) : 0ull;
         }
         int my_e = -1;
+        float my_l = 0.0f;   // its logit, from the key
         if (E <= kRankMax) {
             // rank of each key = number of keys above it (keys are distinct: they
             // carry the index); the keys of ranks 0..k-1 are the top k in order
@@ -77,18 +87,36 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
                 if (lane + 64 * j < E) keys_s[w][lane + 64 * j] = key[j];
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            // eight keys per pass, read before any compare: one LDS latency per
+            // pass instead of one per key
             int rank[kRankMax / 64] = {};
-            for (int q = 0; q < E; ++q) {
+            int q = 0;
+            for (; q + 8 <= E; q += 8) {
+                uint64_t o[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) o[u] = keys_s[w][q + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int j = 0; j < kRankMax / 64; ++j) rank[j] += o[u] > key[j] ? 1 : 0;
+            }
+            for (; q < E; ++q) {
                 const uint64_t o = keys_s[w][q];
 #pragma unroll
                 for (int j = 0; j < kRankMax / 64; ++j) rank[j] += o > key[j] ? 1 : 0;
             }
 #pragma unroll
             for (int j = 0; j < kRankMax / 64; ++j)
-                if (lane + 64 * j < E && rank[j] < k) sel_s[w][rank[j]] = lane + 64 * j;
+                if (lane + 64 * j < E && rank[j] < k) {
+                    sel_s[w][rank[j]] = lane + 64 * j;
+                    sell_s[w][rank[j]] = route_key_logit(key[j]);
+                }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
-            if (lane < k) my_e = sel_s[w][lane];
+            if (lane < k) {
+                my_e = sel_s[w][lane];
+                my_l = sell_s[w][lane];
+            }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();   // the next token's writes come after these reads
         } else {
@@ -100,14 +128,14 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 #pragma unroll
                 for (int j = 0; j < kMaxExperts / 64; ++j)
                     if (key[j] == best) key[j] = 0ull;
-                if (lane == r) my_e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+                if (lane == r) {
+                    my_e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+                    my_l = route_key_logit(best);
+                }
             }
         }
         double lr = -INFINITY;
-        if (lane < k) {
-            const float l = p.logits[(size_t)t * E + my_e];
-            lr = (l != l) ? -INFINITY : (double)l;
-        }
+        if (lane < k) lr = (my_l != my_l) ? -INFINITY : (double)my_l;
         const double l0 = __shfl(lr, 0);
         const double ex = (lane < k) ? ((lr == l0) ? 1.0 : exp(lr - l0)) : 0.0;
         double sum = 0.0;
