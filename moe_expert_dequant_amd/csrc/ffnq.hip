@@ -650,6 +650,29 @@ bool launch_gu_tiled2(const KConfig& a, const GUParams& pa, const KConfig& b, co
     return false;
 }
 
+#define FFNQ_DNT2_CASE(NT_, MT_)                                                                             \
+    if (a.nt == NT_ && a.mt == MT_) {                                                                        \
+        hipExtLaunchKernelGGL((down_tiled_kernel2<FMT_INT4, NT_, MT_>), dim3(na + nb), dim3(64 * a.ks), lds, stream, \
+                              phase_event(2), phase_event(3), 0, qa, qb, na);                                \
+        return true;                                                                                         \
+    }
+
+// Shared and routed tiled INT4 down in one launch (both with the K split).
+bool launch_down_tiled2(const KConfig& a, const DownParams& pa, const KConfig& b, const DownParams& pb,
+                        hipStream_t stream)
+{
+    if (a.nt != b.nt || a.mt != b.mt || a.ks != b.ks || a.ts || b.ts) return false;
+    DownParams qa = pa, qb = pb;
+    qa.ks = a.ks;
+    qa.grid = a.grid;
+    qb.ks = b.ks;
+    qb.grid = b.grid;
+    const int na = a.grid * a.kg, nb = b.grid * b.kg;
+    const size_t lds = std::max(a.lds, b.lds);
+    FFNQ_DNT2_CASE(1, 2) FFNQ_DNT2_CASE(1, 4) FFNQ_DNT2_CASE(2, 4) FFNQ_DNT2_CASE(4, 4)
+    return false;
+}
+
 // The routed half on a checked call (m > 0; the routed workspace at base).
 int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
                const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
@@ -720,17 +743,35 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
         dps = dense_down_params(sh->ffn, hidden, sh->inter, m, dcs, gps.act_out, nullptr,
                                 reinterpret_cast<float*>(sh->base + Ls.part),
                                 reinterpret_cast<const float*>(sh->base + Ls.logit), TAIL_PART);
-        const int sdfmt = to_fmt(sh->ffn->down.fmt);
-        if (!(is_tiled(sh->ffn->down.fmt) ? launch_down_tiled(sdfmt, dcs, stream, dps)
-                                          : launch_down(sdfmt, dcs, 1, hidden, stream, dps)))
-            return FFNQ_ERR_UNSUPPORTED;
-        if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
     }
 
     // phase 2: down per union entry and tile, d_p to pair_out
     const KConfig dc = tiled ? down_tiled_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus, false,
                                                  rows_per_item(false, m, top_k, n_experts), false)
                              : down_config(experts->down.fmt, moe_inter, hidden, u_est, m, cus);
+
+    // Both downs tiled INT4 and the routed one a K split with one wave per
+    // workgroup: the shared down takes the same shape (its K ranges, and so its
+    // partials, unchanged; one K range per workgroup) and both run in one launch.
+    bool merged = false;
+    KConfig dcs1 = dcs;
+    if (sh && tiled && is_tiled(sh->ffn->down.fmt) && is_int4(sh->ffn->down.fmt) && !dc.ts && dc.ks == 1 &&
+        dcs.nt == dc.nt && dcs.mt == dc.mt) {
+        const TileGeo gs = tile_geo(FMT_INT4, hidden, sh->inter);
+        dcs1.ts = 0;
+        dcs1.ks = 1;
+        dcs1.grid = (int)std::min<long long>(gs.T, (long long)cus * 16);
+        dcs1.lds = tiled_launch_lds(1, FMT_INT4, hidden, sh->inter, dcs1.kg, dcs1.rows_cap, 1,
+                                    2 * dcs1.nt * red_lanes(dcs1.nt, dcs1.rows_cap)).total;
+        merged = dcs1.lds <= kLdsBudget;
+    }
+    if (sh && !merged) {
+        const int sdfmt = to_fmt(sh->ffn->down.fmt);
+        if (!(is_tiled(sh->ffn->down.fmt) ? launch_down_tiled(sdfmt, dcs, stream, dps)
+                                          : launch_down(sdfmt, dcs, 1, hidden, stream, dps)))
+            return FFNQ_ERR_UNSUPPORTED;
+        if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    }
     DownParams dp{};
     dp.down = mat_dev(experts->down);
     dp.N = hidden;
@@ -750,8 +791,12 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
         dp.tdown = static_cast<const uint8_t*>(experts->down.q);
         dp.tebytes = tiled_expert_bytes(experts->down);
     }
-    if (!(tiled ? launch_down_tiled(FMT_INT4, dc, stream, dp) : launch_down(FMT_INT4, dc, u_est, hidden, stream, dp)))
+    if (merged) {
+        if (!launch_down_tiled2(dcs1, dps, dc, dp, stream)) return FFNQ_ERR_UNSUPPORTED;
+    } else if (!(tiled ? launch_down_tiled(FMT_INT4, dc, stream, dp)
+                       : launch_down(FMT_INT4, dc, u_est, hidden, stream, dp))) {
         return FFNQ_ERR_UNSUPPORTED;
+    }
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     // seeded rank-ordered reduce + residual

@@ -634,11 +634,12 @@ struct DownParams {
     int ks, grid;              // tiled kernels: waves per workgroup and gridDim.x, as launched
 };
 
-__device__ __forceinline__ void down_finish(const DownParams& p, int t, int n, float h)
+// by: the K range whose partial sum h is.
+__device__ __forceinline__ void down_finish(const DownParams& p, int by, int t, int n, float h)
 {
     if (p.KG > 1 || p.tail == TAIL_PAIR || p.tail == TAIL_RMSNORM || p.tail == TAIL_PART) {
         const size_t rows = p.tail == TAIL_PAIR ? (size_t)p.act_rows : (size_t)p.m;
-        p.part[((size_t)blockIdx.y * rows + t) * p.N + n] = h;
+        p.part[((size_t)by * rows + t) * p.N + n] = h;
     } else if (p.tail == TAIL_RESIDUAL) {
         uint16_t* o = p.out + (size_t)t * p.N + n;
         *o = bf16_from_f64((double)bf16_f32(*o) + (double)h);
@@ -741,7 +742,7 @@ __global__ void __launch_bounds__(512) down_kernel(DownParams p)
                     trow = item_pair(pv, it, li, p.act_rows);
                     if (trow < 0) continue;
                 }
-                down_finish(p, trow, n, h);
+                down_finish(p, blockIdx.y, trow, n, h);
             }
             __syncthreads();
         }

@@ -846,8 +846,9 @@ __global__ void __launch_bounds__(512) gu_tiled_kernel2(GUParams a, GUParams b)
 
 // down + tail: h per (token or pair, hidden row), finished by down_finish
 // (tail, or fp32 partials when K is split or for the routed and RMSNorm tails).
+// bx, by: the workgroup's position along x (tiles) and y (K range).
 template <int FMT, int NT, int MT, bool TS>
-__global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
+__device__ __forceinline__ void down_tiled_run(const DownParams& p, int bx, int by)
 {
     asm volatile("" ::"s"(p.tdown), "s"(p.tebytes), "s"(p.N), "s"(p.K), "s"(p.KG), "s"(p.act), "s"(p.rows_cap),
                  "s"(p.plan), "s"(p.m), "s"(p.top_k), "s"(p.act_rows), "s"(p.topk_ids), "s"(p.n_experts), "s"(p.tail),
@@ -871,8 +872,8 @@ __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
     J.n_experts = p.n_experts;
     J.KS = p.ks;
     J.G = p.grid;
-    J.bx = blockIdx.x;
-    J.by = blockIdx.y;
+    J.bx = bx;
+    J.by = by;
     auto rows = [&](const Item& it, int c0, int t, long long* roff, int* orows) {
         const int xr = c0 + t, li = xr >> 1;
         int arow = li;
@@ -880,8 +881,31 @@ __global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
         roff[t] = (long long)(2 * (arow < 0 ? 0 : arow) + (xr & 1)) * J.K;
         if ((t & 1) == 0) orows[t >> 1] = arow;
     };
-    auto finish = [&](int orow, int n, const float (&v)[1]) { down_finish(p, orow, n, v[0]); };
+    auto finish = [&](int orow, int n, const float (&v)[1]) { down_finish(p, by, orow, n, v[0]); };
     tiled_body<FMT, 1, NT, MT, true, TS>(J, rows, finish);
+}
+
+template <int FMT, int NT, int MT, bool TS>
+__global__ void __launch_bounds__(512) down_tiled_kernel(DownParams p)
+{
+    down_tiled_run<FMT, NT, MT, TS>(p, blockIdx.x, blockIdx.y);
+}
+
+// Two down jobs in one launch (a layer's shared expert and its routed experts),
+// both with the K split: workgroups [0, na) run job a, laid out as a.grid
+// workgroups along x for each of its K ranges; the rest run job b likewise.
+// The jobs share the template shape and the waves per workgroup; each lays out
+// its own LDS within the launch's allocation.
+template <int FMT, int NT, int MT>
+__global__ void __launch_bounds__(512) down_tiled_kernel2(DownParams a, DownParams b, int na)
+{
+    const int bid = (int)blockIdx.x;
+    if (bid < na) {
+        down_tiled_run<FMT, NT, MT, false>(a, bid % a.grid, bid / a.grid);
+    } else {
+        const int r = bid - na;
+        down_tiled_run<FMT, NT, MT, false>(b, r % b.grid, r / b.grid);
+    }
 }
 
 }  // namespace ffnq
