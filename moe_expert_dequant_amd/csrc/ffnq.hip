@@ -550,7 +550,7 @@ int run_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int ta
 
     if (tail == FFNQ_TAIL_RMSNORM) {
         const size_t row_lds = hidden <= kRowLds ? (size_t)hidden * 6 : 0;
-        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), row_lds, stream, dp.part, dc.kg, m, aux, out, hidden,
+        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(kNormThreads), row_lds, stream, dp.part, dc.kg, m, aux, out, hidden,
                            eps);
         if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
     } else if (dc.kg > 1) {

@@ -49,19 +49,21 @@ __device__ __forceinline__ float sum_parts8(const float* part, int R, size_t str
 //   out[t][i] = bf16(h[t][i] / sqrt(mean_i h^2 + eps) * w[i])
 // ([gemma4/shared_expert.rs] encode_rms_norm_bf16w with RMS_EPS).  The sum
 // of squares, the scale and the product are formed in double; the result is
-// rounded to bf16 once.  One workgroup per row.  With `held` (rows of at most
-// kRowLds values) the summed row and the weight are kept in dynamic LDS between
-// the two passes, loaded together in the first; the host launches with n * 6
-// bytes of LDS then.
+// rounded to bf16 once.  One workgroup of kNormThreads per row, so that a row of
+// up to 4 * kNormThreads values is summed from its K-range partials in one
+// round of loads.  With `held` (rows of at most kRowLds values) the summed row
+// and the weight are kept in dynamic LDS between the two passes, loaded
+// together in the first; the host launches with n * 6 bytes of LDS then.
 constexpr int kRowLds = 8192;
+constexpr int kNormThreads = 1024;
 
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ part, int R, int m,
-                                                      const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
-                                                      int n, float eps)
+__global__ void __launch_bounds__(kNormThreads) rmsnorm_kernel(const float* __restrict__ part, int R, int m,
+                                                               const uint16_t* __restrict__ w,
+                                                               uint16_t* __restrict__ out, int n, float eps)
 {
     extern __shared__ float hrow[];   // [n] summed row, then [n] bf16 weight
     uint16_t* wrow = (uint16_t*)(hrow + n);
-    __shared__ double partial[256 / 64];
+    __shared__ double partial[kNormThreads / 64];
     const int t = blockIdx.x, tid = threadIdx.x;
     const size_t stride = (size_t)m * n;
     const bool held = n <= kRowLds;
@@ -69,18 +71,18 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
     // four elements per step, their loads together (indices clamped into the
     // row; only elements < n are kept), added to ss in element order
     auto first_pass = [&](auto sumf) {
-        for (int i0 = tid; i0 < n; i0 += 4 * 256) {
+        for (int i0 = tid; i0 < n; i0 += 4 * kNormThreads) {
             float h4[4];
             uint16_t w4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int ic = min(i0 + 256 * u, n - 1);
+                const int ic = min(i0 + kNormThreads * u, n - 1);
                 h4[u] = sumf((size_t)t * n + ic);
                 w4[u] = w[ic];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int i = i0 + 256 * u;
+                const int i = i0 + kNormThreads * u;
                 if (i < n) {
                     hrow[i] = h4[u];
                     wrow[i] = w4[u];
