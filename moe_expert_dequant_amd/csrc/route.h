@@ -16,6 +16,8 @@ constexpr int kMaxExperts = 1024;   // logits per token held in registers: 16 pe
 constexpr int kMaxSlots = 32;
 constexpr int kIdsCache = 4096;      // pairs whose expert ids the plan pass reads from LDS
 constexpr int kRankMax = 256;        // experts up to which the top-k is found by ranking in LDS
+constexpr int kLgCache = 4096;       // logits (m * E) staged in LDS before the top-k
+constexpr int kParPlan = 64;         // pairs from which the one-sub-batch plan is built in parallel
 
 struct RouteParams {
     const float* logits;    // [m][E]
@@ -54,14 +56,21 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return v;
 }
 
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
 __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 {
     __shared__ int slot_of[kMaxExperts];
     __shared__ int cur_union[kMaxSlots];
+    __shared__ int wsum_s[256 / 64];
     __shared__ int ids_s[kIdsCache];
     __shared__ uint64_t keys_s[256 / 64][kRankMax];   // per wave: the token's keys
     __shared__ int sel_s[256 / 64][kRankMax];         // per wave: expert of each rank < k
     __shared__ float sell_s[256 / 64][kRankMax];      // per wave: logit of each rank < k
+    __shared__ float lg_s[kLgCache];                  // the batch's logits, when they fit
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
     const int m = p.m, k = p.k, E = p.E;
     const int nj = (E + 63) >> 6;
@@ -70,12 +79,21 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     auto id_of = [&](int pp) { return cached ? ids_s[pp] : p.ids[pp]; };
 
     // ---- top-k and weights, one token per wave ----
+    // the batch's logits go to LDS in one round of coalesced loads when they fit,
+    // so that a wave's tokens do not each wait for their own global loads
+    const bool lg_cached = (long long)m * E <= kLgCache;
+    if (lg_cached) {
+        for (int i = tid; i < m * E; i += blockDim.x) lg_s[i] = p.logits[i];
+        __syncthreads();
+    }
     for (int t = w; t < m; t += nw) {
         uint64_t key[kMaxExperts / 64];
 #pragma unroll
         for (int j = 0; j < kMaxExperts / 64; ++j) {
             const int e = lane + 64 * j;
-            key[j] = (j < nj && e < E) ? route_key(p.logits[(size_t)t * E + e], e) : 0ull;
+            key[j] = (j < nj && e < E)
+                         ? route_key(lg_cached ? lg_s[t * E + e] : p.logits[(size_t)t * E + e], e)
+                         : 0ull;
         }
         int my_e = -1;
         float my_l = 0.0f;   // its logit, from the key
@@ -87,30 +105,42 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
                 if (lane + 64 * j < E) keys_s[w][lane + 64 * j] = key[j];
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
-            // eight keys per pass, read before any compare: one LDS latency per
-            // pass instead of one per key
-            int rank[kRankMax / 64] = {};
-            int q = 0;
-            for (; q + 8 <= E; q += 8) {
-                uint64_t o[8];
+            // eight keys per pass, read before any compare; only the NJ key
+            // registers that hold experts are ranked (the 64-bit compares are
+            // the cost of this step)
+            auto rank_keys = [&](auto njc) {
+                constexpr int NJ = decltype(njc)::value;
+                int rank[NJ] = {};
+                int q = 0;
+                for (; q + 8 <= E; q += 8) {
+                    uint64_t o[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) o[u] = keys_s[w][q + u];
+                    for (int u = 0; u < 8; ++u) o[u] = keys_s[w][q + u];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 8; ++u)
 #pragma unroll
-                    for (int j = 0; j < kRankMax / 64; ++j) rank[j] += o[u] > key[j] ? 1 : 0;
-            }
-            for (; q < E; ++q) {
-                const uint64_t o = keys_s[w][q];
-#pragma unroll
-                for (int j = 0; j < kRankMax / 64; ++j) rank[j] += o > key[j] ? 1 : 0;
-            }
-#pragma unroll
-            for (int j = 0; j < kRankMax / 64; ++j)
-                if (lane + 64 * j < E && rank[j] < k) {
-                    sel_s[w][rank[j]] = lane + 64 * j;
-                    sell_s[w][rank[j]] = route_key_logit(key[j]);
+                        for (int j = 0; j < NJ; ++j) rank[j] += o[u] > key[j] ? 1 : 0;
                 }
+                for (; q < E; ++q) {
+                    const uint64_t o = keys_s[w][q];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) rank[j] += o > key[j] ? 1 : 0;
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    if (lane + 64 * j < E && rank[j] < k) {
+                        sel_s[w][rank[j]] = lane + 64 * j;
+                        sell_s[w][rank[j]] = route_key_logit(key[j]);
+                    }
+            };
+            if (nj <= 1)
+                rank_keys(IntC<1>{});
+            else if (nj == 2)
+                rank_keys(IntC<2>{});
+            else if (nj == 3)
+                rank_keys(IntC<3>{});
+            else
+                rank_keys(IntC<4>{});
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
             if (lane < k) {
@@ -150,17 +180,70 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 
     // ---- plan: unused entries are -1 ----
     const int total = 2 * m + 4 + 4 * m * k;
+    const int P = m * k;
     for (int i = tid; i < total; i += blockDim.x) p.plan[i] = -1;
-    for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
-    __syncthreads();
-    if (w != 0) return;
-
     int32_t* sub_tok = p.plan + 1;
     int32_t* sub_uni = p.plan + (m + 2);
     int32_t* uexp = p.plan + (2 * m + 3);
     int32_t* pslot = p.plan + (2 * m + 3 + m * k);
     int32_t* spb = p.plan + (2 * m + 3 + 2 * m * k);
     int32_t* sp = p.plan + (2 * m + 4 + 3 * m * k);
+
+    // When the expert union of the whole batch fits the cap, the greedy plan is
+    // one sub-batch of every token, with slots in first-appearance pair order;
+    // that is found in parallel: each expert's first pair (an LDS minimum), then
+    // a scan over the pairs' first-appearance flags.  Otherwise (or when the ids
+    // are not held in LDS) wave 0 walks the tokens in order.
+    int U = kMaxSlots + 1;
+    if (cached && P >= kParPlan) {
+        for (int i = tid; i < E; i += blockDim.x) slot_of[i] = 0x7FFFFFFF;
+        __syncthreads();
+        for (int pp = tid; pp < P; pp += blockDim.x) atomicMin(&slot_of[ids_s[pp]], pp);
+        __syncthreads();
+        const int C = (P + (int)blockDim.x - 1) / (int)blockDim.x;   // pairs per thread (<= 16)
+        const int b0 = min(P, tid * C), b1 = min(P, b0 + C);
+        unsigned firsts = 0u;
+        int cnt = 0;
+        for (int pp = b0; pp < b1; ++pp)
+            if (slot_of[ids_s[pp]] == pp) {
+                firsts |= 1u << (pp - b0);
+                ++cnt;
+            }
+        int incl = cnt;   // inclusive scan over the wave, then over the waves
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wsum_s[w] = incl;
+        __syncthreads();   // every flag is read before slot_of is overwritten below
+        int wbase = 0;
+        U = 0;
+        for (int i = 0; i < nw; ++i) {
+            wbase += i < w ? wsum_s[i] : 0;
+            U += wsum_s[i];
+        }
+        if (U <= p.cap) {
+            int sl = wbase + incl - cnt;
+            for (int pp = b0; pp < b1; ++pp)
+                if (firsts & (1u << (pp - b0))) {
+                    const int e = ids_s[pp];
+                    slot_of[e] = sl;
+                    cur_union[sl] = e;
+                    uexp[sl] = e;
+                    ++sl;
+                }
+            __syncthreads();
+            for (int pp = tid; pp < P; pp += blockDim.x) pslot[pp] = slot_of[ids_s[pp]];
+        } else {
+            __syncthreads();
+            for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
+        }
+    } else {
+        for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
+    }
+    __syncthreads();
+    if (w != 0) return;
+
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     int S = 0, base = 0, usize = 0, s_tok = 0, pos = 0;
@@ -181,12 +264,11 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
                 if (lane == j) cnt += __popcll(msk);
             }
         }
-        int excl = cnt;   // exclusive prefix over lanes 0..usize-1
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(excl, off);
-            if (lane >= off) excl += o;
+        int excl = 0;   // exclusive prefix over lanes 0..usize-1 (lane reads, no LDS round trips)
+        for (int j = 0, run = 0; j < usize; ++j) {
+            if (lane == j) excl = run;
+            run += __builtin_amdgcn_readlane(cnt, j);
         }
-        excl -= cnt;
         int cur = pos + excl;
         if (lane < usize) spb[base + lane] = cur;
         for (int c = P0; c < P1; c += 64) {
@@ -194,7 +276,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
             const int sl = (pp < P1) ? slot_of[id_of(pp)] : -1;
             for (int j = 0; j < usize; ++j) {
                 const uint64_t msk = __ballot(sl == j);
-                const int start = __shfl(cur, j);
+                const int start = __builtin_amdgcn_readlane(cur, j);
                 if (sl == j) sp[start + __popcll(msk & lt)] = pp;
                 if (lane == j) cur += __popcll(msk);
             }
@@ -206,6 +288,10 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
         __builtin_amdgcn_wave_barrier();
     };
 
+    if (U <= p.cap) {   // one sub-batch, slots assigned above
+        usize = U;
+        s_tok = 0;
+    } else {
     for (int t = 0; t < m; ++t) {
         const int e = (lane < k) ? id_of(t * k + lane) : 0;
         int cur = (lane < k) ? slot_of[e] : 0;
@@ -236,6 +322,7 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
         __builtin_amdgcn_wave_barrier();
         if (lane < k) pslot[(size_t)t * k + lane] = cur;
         usize += nf;
+    }
     }
     close_sub(s_tok, m);
     ++S;

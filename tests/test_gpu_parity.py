@@ -177,7 +177,9 @@ def check_route(logits, k, cap, scale=None, label=""):
 
 @pytest.mark.parametrize("m,E,k,cap", [(1, 8, 2, 32), (4, 128, 8, 32), (4, 128, 8, 12), (2, 128, 8, 16),
                                        (64, 8, 2, 32), (7, 16, 4, 5), (33, 64, 6, 7), (200, 40, 3, 9),
-                                       (5, 1024, 32, 32), (3, 3, 3, 3)])
+                                       (5, 1024, 32, 32), (3, 3, 3, 3),
+                                       # one sub-batch over many pairs (parallel plan), and past the LDS id cache
+                                       (300, 8, 2, 32), (1000, 16, 4, 32), (1100, 16, 4, 32), (64, 128, 8, 32)])
 def test_route_random(m, E, k, cap):
     logits = gen.router_logits(gen.tensor_key(m * 1000 + E, k), m, E)
     check_route(logits, k, cap, label="random")
