@@ -902,7 +902,11 @@ int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_
     if (plan_bytes < (size_t)FFNQ_PLAN_INTS((size_t)m, (size_t)top_k) * 4) return FFNQ_ERR_WORKSPACE;
     if (m == 0) return FFNQ_OK;
     RouteParams p{logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan};
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(256), 0, stream, p);
+    const bool small = (long long)m * top_k <= kIdsCache && (long long)m * n_experts <= kLgCache;
+    if (small)
+        hipLaunchKernelGGL(route_kernel<true>, dim3(1), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(route_kernel<false>, dim3(1), dim3(256), 0, stream, p);
     return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
 }
 

@@ -61,6 +61,11 @@ struct IntC {
     static constexpr int value = N;
 };
 
+// SMALL: the batch's logits (m * E <= kLgCache) and chosen ids (m * k <=
+// kIdsCache) are held in LDS; a compile-time choice, because a run-time select
+// between an LDS and a global source compiles to one flat load, and a flat load
+// waits for every global store of the wave before it returns.
+template <bool SMALL>
 __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 {
     __shared__ int slot_of[kMaxExperts];
@@ -75,14 +80,18 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     const int m = p.m, k = p.k, E = p.E;
     const int nj = (E + 63) >> 6;
     // the plan pass reads the chosen experts back: from LDS when they fit
-    const bool cached = (long long)m * k <= kIdsCache;
-    auto id_of = [&](int pp) { return cached ? ids_s[pp] : p.ids[pp]; };
+    constexpr bool cached = SMALL;
+    auto id_of = [&](int pp) {
+        if constexpr (SMALL)
+            return ids_s[pp];
+        else
+            return p.ids[pp];
+    };
 
     // ---- top-k and weights, one token per wave ----
     // the batch's logits go to LDS in one round of coalesced loads when they fit,
     // so that a wave's tokens do not each wait for their own global loads
-    const bool lg_cached = (long long)m * E <= kLgCache;
-    if (lg_cached) {
+    if constexpr (SMALL) {
         for (int i = tid; i < m * E; i += blockDim.x) lg_s[i] = p.logits[i];
         __syncthreads();
     }
@@ -91,9 +100,14 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 #pragma unroll
         for (int j = 0; j < kMaxExperts / 64; ++j) {
             const int e = lane + 64 * j;
-            key[j] = (j < nj && e < E)
-                         ? route_key(lg_cached ? lg_s[t * E + e] : p.logits[(size_t)t * E + e], e)
-                         : 0ull;
+            float l = 0.0f;
+            if (j < nj && e < E) {
+                if constexpr (SMALL)
+                    l = lg_s[t * E + e];
+                else
+                    l = p.logits[(size_t)t * E + e];
+            }
+            key[j] = (j < nj && e < E) ? route_key(l, e) : 0ull;
         }
         int my_e = -1;
         float my_l = 0.0f;   // its logit, from the key
