@@ -18,6 +18,7 @@ constexpr int kIdsCache = 4096;      // pairs whose expert ids the plan pass rea
 constexpr int kRankMax = 256;        // experts up to which the top-k is found by ranking in LDS
 constexpr int kLgCache = 4096;       // logits (m * E) staged in LDS before the top-k
 constexpr int kParPlan = 64;         // pairs from which the one-sub-batch plan is built in parallel
+constexpr int kPairPlan = 64;        // pairs up to which it is built one pair per thread, CSR included
 
 struct RouteParams {
     const float* logits;    // [m][E]
@@ -71,6 +72,8 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     __shared__ int slot_of[kMaxExperts];
     __shared__ int cur_union[kMaxSlots];
     __shared__ int wsum_s[256 / 64];
+    __shared__ int pl_s[kPairPlan];                   // per pair: first-appearance flag, then slot
+    __shared__ int sst_s[kMaxSlots];                  // per slot: first position in the CSR
     __shared__ int ids_s[kIdsCache];
     __shared__ uint64_t keys_s[256 / 64][kRankMax];   // per wave: the token's keys
     __shared__ int sel_s[256 / 64][kRankMax];         // per wave: expert of each rank < k
@@ -209,7 +212,53 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     // a scan over the pairs' first-appearance flags.  Otherwise (or when the ids
     // are not held in LDS) wave 0 walks the tokens in order.
     int U = kMaxSlots + 1;
-    if (cached && P >= kParPlan) {
+    bool done = false;   // the whole plan is written (one sub-batch, pair-per-thread path)
+    if (cached && P <= kPairPlan) {
+        // one pair per thread; every count is a loop over earlier pairs in LDS
+        // (the same address in every lane of a step)
+        for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
+        const int e = tid < P ? ids_s[tid] : -1;
+        int first = tid < P ? 1 : 0;
+#pragma unroll 8
+        for (int q = 0; q < tid && q < P; ++q) first &= ids_s[q] != e;
+        if (tid < kPairPlan) pl_s[tid] = first;
+        U = __syncthreads_count(first);
+        if (U <= p.cap) {
+            if (first) {   // slot = first appearances before this pair
+                int sl = 0;
+#pragma unroll 8
+                for (int q = 0; q < tid; ++q) sl += pl_s[q];
+                slot_of[e] = sl;
+                cur_union[sl] = e;
+                uexp[sl] = e;
+            }
+            __syncthreads();
+            const int my = tid < P ? slot_of[e] : -1;
+            if (tid < P) {
+                pslot[tid] = my;
+                pl_s[tid] = my;
+            }
+            __syncthreads();
+            if (tid < U) {   // slot starts: pairs in earlier slots
+                int st = 0;
+#pragma unroll 8
+                for (int q = 0; q < P; ++q) st += pl_s[q] < tid ? 1 : 0;
+                sst_s[tid] = st;
+                spb[tid] = st;
+            }
+            __syncthreads();
+            if (tid < P) {   // the pair's place among its slot's pairs, ascending
+                int r = 0;
+#pragma unroll 8
+                for (int q = 0; q < tid; ++q) r += pl_s[q] == my ? 1 : 0;
+                sp[sst_s[my] + r] = tid;
+            }
+            done = true;
+        }
+        __syncthreads();
+        if (!done)
+            for (int i = tid; i < E; i += blockDim.x) slot_of[i] = -1;
+    } else if (cached && P >= kParPlan) {
         for (int i = tid; i < E; i += blockDim.x) slot_of[i] = 0x7FFFFFFF;
         __syncthreads();
         for (int pp = tid; pp < P; pp += blockDim.x) atomicMin(&slot_of[ids_s[pp]], pp);
@@ -264,7 +313,14 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     if (lane == 0) {
         sub_tok[0] = 0;
         sub_uni[0] = 0;
+        if (done) {
+            sub_tok[1] = m;
+            sub_uni[1] = U;
+            spb[U] = P;
+            p.plan[0] = 1;
+        }
     }
+    if (done) return;
 
     // CSR of the sub-batch [t0, t1): pairs grouped by slot, ascending.
     auto close_sub = [&](int t0, int t1) {
