@@ -48,6 +48,15 @@ __device__ __forceinline__ float route_key_logit(uint64_t key)
     return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
+// v of lane `src` (uniform), by lane reads rather than a shuffle through LDS.
+__device__ __forceinline__ double read_lane_f64(double v, int src)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
     for (int off = 32; off > 0; off >>= 1) {
@@ -183,10 +192,10 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
         }
         double lr = -INFINITY;
         if (lane < k) lr = (my_l != my_l) ? -INFINITY : (double)my_l;
-        const double l0 = __shfl(lr, 0);
+        const double l0 = read_lane_f64(lr, 0);
         const double ex = (lane < k) ? ((lr == l0) ? 1.0 : exp(lr - l0)) : 0.0;
         double sum = 0.0;
-        for (int r = 0; r < k; ++r) sum += __shfl(ex, r);
+        for (int r = 0; r < k; ++r) sum += read_lane_f64(ex, r);
         if (lane < k) {
             const double sc = p.scale ? (double)p.scale[my_e] : 1.0;
             p.ids[(size_t)t * k + lane] = my_e;
