@@ -62,6 +62,7 @@ def lib():
             "or_rmsnorm_row": (None, [vp, vp, i32, f32, vp]),
             "or_gate_logit": (f32, [vp, vp, i32]),
             "or_sigmoid_gate": (C.c_uint16, [f32, f32]),
+            "or_router_logits": (None, [vp, vp, i32, i32, i32, vp]),
             "or_dense": (i32, [P, P, P, i32, i32, i32, i32, i32, vp, vp, vp, f32]),
             "or_shared_expert": (i32, [P, P, P, i32, i32, i32, i32, i32, vp, vp, vp, f32]),
             "or_topk_token": (None, [vp, vp, i32, i32, vp, vp]),
@@ -156,6 +157,17 @@ def gate_logit(wg_bits: np.ndarray, x_bits: np.ndarray) -> float:
     wg = _c(wg_bits, np.uint16)
     x = _c(x_bits, np.uint16)
     return lib().or_gate_logit(_p(wg), _p(x), wg.shape[0])
+
+
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """logits [m][E] fp32 = x bf16 [m][hidden] times the router weight bf16 [E][hidden] (rows)."""
+    x = _c(x_bits, np.uint16)
+    w = _c(w_bits, np.uint16)
+    m, hidden = x.shape
+    E = w.shape[0]
+    out = np.empty((m, E), dtype=np.float32)
+    lib().or_router_logits(_p(x), _p(w), m, hidden, E, _p(out))
+    return out
 
 
 def sigmoid_gate(h: float, logit: float) -> int:

@@ -188,6 +188,21 @@ float or_gate_logit(const uint16_t* wg, const uint16_t* x, int n)
     return (float)acc;
 }
 
+/* Router logits ([qwen/moe_batch.rs] `encode_qwen_layer_moe_batched`: the M
+ * router GEMVs run before the routed half, which reads their fp32 logits
+ * back): logits[t][e] = <w_e, x_t> over hidden, each in double, rounded once
+ * to fp32.  x bf16 [m][hidden], w bf16 [n_experts][hidden]. */
+void or_router_logits(const uint16_t* x, const uint16_t* w, int m, int hidden, int n_experts, float* logits)
+{
+    for (int t = 0; t < m; ++t)
+        for (int e = 0; e < n_experts; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < hidden; ++i)
+                acc += or_bf16_value(w[(size_t)e * hidden + i]) * or_bf16_value(x[(size_t)t * hidden + i]);
+            logits[(size_t)t * n_experts + e] = (float)acc;
+        }
+}
+
 /* h * sigmoid(logit) ([qwen/moe_batch.rs] `encode_sigmoid_scalar_mul`). */
 uint16_t or_sigmoid_gate(float h, float logit)
 {

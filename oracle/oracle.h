@@ -43,6 +43,7 @@ uint16_t or_residual(uint16_t x, float h);
 void or_rmsnorm_row(const float* h, const uint16_t* w, int n, float eps, uint16_t* out);
 float or_gate_logit(const uint16_t* wg, const uint16_t* x, int n);
 uint16_t or_sigmoid_gate(float h, float logit);
+void or_router_logits(const uint16_t* x, const uint16_t* w, int m, int hidden, int n_experts, float* logits);
 int or_dense(const or_qmat* gate, const or_qmat* up, const or_qmat* down, int hidden, int inter, int m,
              int act, int tail, const uint16_t* x, uint16_t* out, const uint16_t* norm_w, float eps);
 int or_shared_expert(const or_qmat* gate, const or_qmat* up, const or_qmat* down, int hidden, int inter,

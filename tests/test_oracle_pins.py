@@ -173,6 +173,32 @@ def test_gate_logit_exact_integers():
     assert got == float(np.dot(a, b))
 
 
+def test_router_logits_selection_hand_and_constant():
+    # a selection router: row e of the weight is 1.0 at input pi(e), so logits[t][e] = x[t][pi(e)]
+    # exactly (a transposed operand or a wrong row/column index fails)
+    rng = np.random.default_rng(7)
+    m, hidden, E = 3, 64, 16
+    x = gen.bf16_bits(rng.standard_normal((m, hidden)))
+    pi = rng.permutation(hidden)[:E]
+    w = np.zeros((E, hidden), np.uint16)
+    w[np.arange(E), pi] = gen.bf16_bits(1.0)
+    got = oracle.router_logits(x, w)
+    assert got.shape == (m, E)
+    assert np.array_equal(got, gen.bf16_to_f32(x[:, pi]))
+    # by hand: x = (1, 2, 3, 4, 0, ...), rows (1, 1, 1, 1, 0, ...) and (0.5, -1, 2, 0, ...) give 10 and 4.5
+    x1 = np.zeros((1, 8), np.uint16)
+    x1[0, :4] = gen.bf16_bits([1.0, 2.0, 3.0, 4.0])
+    w1 = np.zeros((2, 8), np.uint16)
+    w1[0, :4] = gen.bf16_bits([1.0, 1.0, 1.0, 1.0])
+    w1[1, :3] = gen.bf16_bits([0.5, -1.0, 2.0])
+    assert oracle.router_logits(x1, w1).tolist() == [[10.0, 4.5]]
+    # constant rows against an all-ones token: hidden * 2^-e, exact
+    hidden = 2048
+    ones = np.full((1, hidden), gen.bf16_bits(1.0), np.uint16)
+    wc = np.stack([np.full(hidden, gen.bf16_bits(2.0 ** -e), np.uint16) for e in range(6)])
+    assert oracle.router_logits(ones, wc)[0].tolist() == [hidden * 2.0 ** -e for e in range(6)]
+
+
 # ---------------------------------------------------------------------------
 # O5 router
 
