@@ -267,6 +267,7 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
         counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
         extra = dict(union=union, sub_batches=n_sub, tokens_per_expert_min=int(counts[counts > 0].min()),
                      tokens_per_expert_max=int(counts.max()))
+        extra["router_gemv_us"] = time_router_gemv(x, m, hidden, E)
         io = 2 * m * hidden + 4 * m * E + 4 * m * hidden                 # x; logits; residual read and written
         bytes_of = lambda: touched + io
     for i in range(warmup):
@@ -285,6 +286,30 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
     return dict(call_us_median=med * 1e6, call_us_p10=float(np.percentile(t, 10)) * 1e6,
                 call_us_p90=float(np.percentile(t, 90)) * 1e6, tokens_per_s=m / med, bytes_per_call=nb,
                 achieved_GBs=nb / med / 1e9, frac_of_peak=nb / med / 1e9 / HBM_PEAK_GBS, weight_copies=copies, **extra)
+
+
+def time_router_gemv(x, m: int, hidden: int, E: int, calls: int = 50) -> float:
+    """Time per call (us) of the router GEMV in front of the top-k (ffnq_router_logits) on a seeded bf16
+    router weight [E][hidden] (N(0,1)/sqrt(hidden)): `calls` back-to-back calls between two HIP events, so
+    that the events' own cost is spread (a single short kernel between two events mostly times the events).
+    Not part of the layer figures, whose workload takes the logits as input."""
+    import torch
+    import gen
+    import moe_expert_dequant_amd as fq
+
+    rng = np.random.default_rng(1000 + E)
+    w = _dev16(gen.bf16_bits(rng.standard_normal((E, hidden)) / np.sqrt(hidden)))
+    lg = torch.empty((m, E), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        fq.router_logits(x, w, m, hidden, E, lg)
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(calls):
+        fq.router_logits(x, w, m, hidden, E, lg)
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) * 1e3 / calls
 
 
 def run_configs(steps: int, warmup: int) -> dict:

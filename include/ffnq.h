@@ -187,6 +187,25 @@ FFNQ_API int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int 
                        const uint16_t* x, uint16_t* h_out, const uint16_t* aux, float eps,
                        void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/* ---- ffnq_router_logits --------------------------------------------------------
+ * The router GEMV in front of ffnq_moe_route ([qwen/moe_batch.rs]
+ * `encode_qwen_layer_moe_batched`: the M router GEMVs run before the routed
+ * half, which reads their fp32 logits back):
+ *     logits[t][e] = sum_i w[e][i] * x[t][i]
+ * with bf16 operands (exact in fp32) and fp32 products and sums; the order of
+ * the sum is the library's own (results are within fp32 reassociation of the
+ * exact dot product, not bit-equal to any particular order).
+ * x:      device, bf16 [m][hidden], token-major (the rows ffnq_moe_layer reads).
+ * w:      device, bf16 [n_experts][hidden], the router weight, row-major.
+ * logits: device, fp32 [m][n_experts], written (the input of ffnq_moe_route).
+ * All pointers 16-byte aligned; hidden a multiple of 8; logits must not
+ * overlap x or w.  Asynchronous on `stream`; m == 0 is a no-op.
+ * Errors: INVALID (NULL pointers, m < 0, hidden <= 0 or not a multiple of 8,
+ * n_experts <= 0, misalignment, overlap, sizes past the library's limits),
+ * HIP (launch failure). */
+FFNQ_API int ffnq_router_logits(const uint16_t* x, const uint16_t* w, int m, int hidden, int n_experts,
+                                float* logits, hipStream_t stream);
+
 /* ---- ffnq_moe_route ----------------------------------------------------------
  * Router top-k and the expert-union plan, entirely on the device
  * ([qwen/moe_batch.rs]: the host top-k over read-back logits with

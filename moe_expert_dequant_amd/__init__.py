@@ -29,7 +29,8 @@ TAIL_SIGMOID_GATE = 3
 
 OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
-EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_moe_layer",
+EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route", "ffnq_moe_routed_batched",
+           "ffnq_moe_layer",
            "ffnq_status_string", "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
 
 
@@ -67,10 +68,12 @@ def lib():
         FP = C.POINTER(Ffn)
         L.ffnq_dense.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
         L.ffnq_shared_expert.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
+        L.ffnq_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.ffnq_moe_route.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
         L.ffnq_moe_routed_batched.argtypes = [FP, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ffnq_moe_layer.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("ffnq_dense", "ffnq_shared_expert", "ffnq_moe_route", "ffnq_moe_routed_batched", "ffnq_moe_layer"):
+        for f in ("ffnq_dense", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route", "ffnq_moe_routed_batched",
+                  "ffnq_moe_layer"):
             getattr(L, f).restype = C.c_int
         L.ffnq_status_string.argtypes = [C.c_int]
         L.ffnq_status_string.restype = C.c_char_p
@@ -182,6 +185,13 @@ def shared_expert(ffn: Ffn, hidden: int, inter: int, m: int, act: int, tail: int
     args = (C.byref(ffn), hidden, inter, m, act, tail, _ptr(x), _ptr(h_out), _ptr(aux), eps)
     buf, n = _ws(L.ffnq_shared_expert, args, ws)
     _check("ffnq_shared_expert", L.ffnq_shared_expert(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+def router_logits(x, w, m: int, hidden: int, n_experts: int, logits, stream=None):
+    """ffnq_router_logits: logits [m][E] fp32 = x bf16 [m][hidden] times the router weight bf16 [E][hidden]."""
+    L = lib()
+    _check("ffnq_router_logits", L.ffnq_router_logits(_ptr(x), _ptr(w), m, hidden, n_experts, _ptr(logits),
+                                                      _stream(stream)))
 
 
 def moe_route(logits, m: int, n_experts: int, top_k: int, slot_cap: int, topk_ids, topk_w, plan,

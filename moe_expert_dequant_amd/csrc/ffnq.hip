@@ -887,6 +887,24 @@ int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int m, int ac
     return dense_common(ffn, hidden, inter, m, act, tail, x, h_out, aux, eps, ws, ws_bytes, stream, true);
 }
 
+int ffnq_router_logits(const uint16_t* x, const uint16_t* w, int m, int hidden, int n_experts, float* logits,
+                       hipStream_t stream)
+{
+    if (!x || !w || !logits) return FFNQ_ERR_INVALID;
+    if (m < 0 || hidden <= 0 || hidden % 8 != 0 || n_experts <= 0) return FFNQ_ERR_INVALID;
+    if (misaligned(x) || misaligned(w) || misaligned(logits)) return FFNQ_ERR_INVALID;
+    if ((long long)m * n_experts > (1LL << 30) || (long long)n_experts * hidden > (1LL << 40)) return FFNQ_ERR_INVALID;
+    const size_t lbytes = (size_t)m * n_experts * 4;
+    if (m > 0 && (overlap(logits, lbytes, x, (size_t)m * hidden * 2) ||
+                  overlap(logits, lbytes, w, (size_t)n_experts * hidden * 2)))
+        return FFNQ_ERR_INVALID;
+    if (m == 0) return FFNQ_OK;
+    const long long waves = (long long)m * n_experts;
+    hipLaunchKernelGGL(router_gemv_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, x, w, m, hidden,
+                       n_experts, logits);
+    return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
+}
+
 int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_experts, int top_k, int slot_cap,
                    int32_t* topk_ids, float* topk_w, int32_t* plan, size_t plan_bytes, hipStream_t stream)
 {

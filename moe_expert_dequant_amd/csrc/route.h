@@ -66,6 +66,50 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return v;
 }
 
+// Router GEMV ([qwen/moe_batch.rs] encode_qwen_layer_moe_batched: the M
+// router GEMVs run before the routed half, which reads their fp32 logits back):
+// logits[t][e] = sum_i w[e][i] * x[t][i], bf16 operands (exact in fp32), fp32
+// products and sums.  One wave per (token, expert): lane l takes inputs
+// 8l .. 8l+7 of every 512 (16-byte loads of both rows, all issued before the
+// adds), then the wave adds its lanes' sums.  hidden is a multiple of 8.
+__global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w, int m, int hidden,
+                                                          int n_experts, float* __restrict__ logits)
+{
+    const int wid = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (wid >= m * n_experts) return;   // whole waves (wid is uniform in a wave)
+    const int t = wid / n_experts, e = wid - t * n_experts;
+    const uint16_t* xr = x + (size_t)t * hidden;
+    const uint16_t* wr = w + (size_t)e * hidden;
+    float acc = 0.0f;
+    int i = lane * 8;
+    for (; i + 3 * 512 < hidden; i += 4 * 512) {
+        u32x4 xv[4], wv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            xv[u] = *(const u32x4*)(xr + i + u * 512);
+            wv[u] = *(const u32x4*)(wr + i + u * 512);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc = fmaf(bf16lo_f32(wv[u][j]), bf16lo_f32(xv[u][j]), acc);
+                acc = fmaf(bf16hi_f32(wv[u][j]), bf16hi_f32(xv[u][j]), acc);
+            }
+    }
+    for (; i < hidden; i += 512) {
+        const u32x4 xv = *(const u32x4*)(xr + i), wv = *(const u32x4*)(wr + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc = fmaf(bf16lo_f32(wv[j]), bf16lo_f32(xv[j]), acc);
+            acc = fmaf(bf16hi_f32(wv[j]), bf16hi_f32(xv[j]), acc);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) logits[(size_t)t * n_experts + e] = acc;
+}
+
 template <int N>
 struct IntC {
     static constexpr int value = N;

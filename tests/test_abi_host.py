@@ -252,3 +252,15 @@ def test_tiled_ffn_checks():
     rc, _ = call_dense(fq.Ffn(fq.QMat(T4, 512, 256, None, None, None), fq.QMat(T4, 512, 256, addr(10), None, None),
                               fq.QMat(T4, 256, 512, addr(20), None, None)))
     assert rc == -1                                           # NULL packed buffer
+
+
+def test_router_logits_refusals():
+    L = fq.lib()
+    x, w, lg = addr(70), addr(71), addr(72)
+    assert L.ffnq_router_logits(None, w, 2, 256, 8, lg, None) == -1           # NULL
+    assert L.ffnq_router_logits(x, w, 2, 250, 8, lg, None) == -1              # hidden not a multiple of 8
+    assert L.ffnq_router_logits(x, w, 2, 256, 0, lg, None) == -1              # no experts
+    assert L.ffnq_router_logits(x, w, -1, 256, 8, lg, None) == -1             # m < 0
+    assert L.ffnq_router_logits(x + 4, w, 2, 256, 8, lg, None) == -1          # misaligned
+    assert L.ffnq_router_logits(x, w, 2, 256, 8, x + 16, None) == -1          # logits overlap x
+    assert L.ffnq_router_logits(x, w, 0, 256, 8, lg, None) == 0               # m == 0: no-op

@@ -185,6 +185,43 @@ def test_route_random(m, E, k, cap):
     check_route(logits, k, cap, label="random")
 
 
+@pytest.mark.parametrize("m,hidden,E", [(1, 2048, 128), (4, 2048, 128), (64, 4096, 8), (3, 264, 17), (5, 4104, 1)])
+def test_router_logits(m, hidden, E):
+    # the router GEMV against the oracle: within fp32 reassociation of the exact dot product
+    rng = np.random.default_rng(m * 7 + E)
+    x = gen.bf16_bits(rng.standard_normal((m, hidden)))
+    w = gen.bf16_bits(rng.standard_normal((E, hidden)) / np.sqrt(hidden))
+    say(f"router_logits m {m} hidden {hidden} E {E}")
+    lg = torch.empty((m, E), dtype=torch.float32, device="cuda")
+    fq.router_logits(dev(x.view(np.int16)), dev(w.view(np.int16)), m, hidden, E, lg)
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy().astype(np.float64)
+    want = oracle.router_logits(x, w).astype(np.float64)
+    # fp32 summation error bound: a chain of at most 8 * ceil(hidden / 512) + 6 roundings (a lane's terms,
+    # 8 per 512 inputs, then the wave's 6-level tree), each at most 2^-24 of a running magnitude <= sum |w x|;
+    # plus the oracle's one rounding of the exact value
+    absdot = np.abs(gen.bf16_to_f32(x)).astype(np.float64) @ np.abs(gen.bf16_to_f32(w)).astype(np.float64).T
+    chain = 8 * ((hidden + 511) // 512) + 6
+    bound = chain * 2.0 ** -24 * absdot + 2.0 ** -24 * np.abs(want)
+    assert np.all(np.abs(got - want) <= bound)
+
+
+def test_router_logits_exact_selection_then_route():
+    # a selection router gives the inputs themselves, bit for bit, and routing them matches the oracle
+    rng = np.random.default_rng(11)
+    m, hidden, E, k, cap = 4, 2048, 128, 8, 32
+    x = gen.bf16_bits(rng.standard_normal((m, hidden)))
+    pi = rng.permutation(hidden)[:E]
+    w = np.zeros((E, hidden), np.uint16)
+    w[np.arange(E), pi] = gen.bf16_bits(1.0)
+    lg = torch.empty((m, E), dtype=torch.float32, device="cuda")
+    fq.router_logits(dev(x.view(np.int16)), dev(w.view(np.int16)), m, hidden, E, lg)
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy()
+    assert np.array_equal(got, oracle.router_logits(x, w))
+    check_route(got, k, cap, label="selection router")
+
+
 def test_route_ties_nan_inf_scale():
     rng = np.random.default_rng(5)
     lg = rng.integers(-2, 3, (16, 12)).astype(np.float32)          # many ties
