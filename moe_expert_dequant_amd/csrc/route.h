@@ -5,8 +5,10 @@
 // read_f32_buffer_at + router_topk_gemma4), then plan sub-batches whose expert
 // union fits the slot cap (next_routed_sub_batch / plan_and_stream_union).
 // Here both steps run in one workgroup so the layer has no host round trip:
-// the waves select each token's experts in parallel, then wave 0 walks the
-// tokens in order to build the greedy union plan.
+// the waves select each token's experts in parallel, then the greedy union
+// plan is built -- in parallel when the whole batch's union fits the cap (one
+// sub-batch), else by wave 0 walking the tokens in order.  The router GEMV
+// that produces the logits (router_gemv_kernel) is a launch of its own.
 #pragma once
 #include "device.h"
 
@@ -261,9 +263,10 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
 
     // When the expert union of the whole batch fits the cap, the greedy plan is
     // one sub-batch of every token, with slots in first-appearance pair order;
-    // that is found in parallel: each expert's first pair (an LDS minimum), then
-    // a scan over the pairs' first-appearance flags.  Otherwise (or when the ids
-    // are not held in LDS) wave 0 walks the tokens in order.
+    // that is found in parallel: up to kPairPlan pairs with one pair per thread
+    // (CSR included), from kParPlan pairs on with each expert's first pair as an
+    // LDS minimum and a scan over the pairs' first-appearance flags.  Otherwise
+    // (or when the ids are not held in LDS) wave 0 walks the tokens in order.
     int U = kMaxSlots + 1;
     bool done = false;   // the whole plan is written (one sub-batch, pair-per-thread path)
     if (cached && P <= kPairPlan) {
