@@ -14,7 +14,9 @@ Uniforms use the top 53 bits; normals use the Box-Muller transform in double;
 bf16 values are rounded from fp32 to nearest even.
 
 Workload recipe (shapes and distributions of the pages' model families):
-  INT8 per-row:     q ~ U{-127..127}, s = 1/(127*sqrt(K)) fp32
+  INT8 per-row:     q ~ U{-127..127}, s = 1/(127*sqrt(K)) fp32 (the workloads' recipe);
+                    row_scales=True draws s_n = U(0.5,1.5)/(127*sqrt(K)) per row instead,
+                    so that a test sees which row's scale a kernel applies
   INT4 affine g64:  codes ~ U{0..15}, s = bf16(U(0.5,1.5)/(8*sqrt(K))), z = bf16(U(6,9))
   x, residual:      bf16(N(0,1)), token-major [M][hidden]
   RMSNorm weight:   bf16(U(0.8,1.2))
@@ -107,11 +109,13 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
 # quantized matrices
 
 
-def qmat(fmt: int, n: int, k: int, key: int, experts: int = 0) -> dict:
+def qmat(fmt: int, n: int, k: int, key: int, experts: int = 0, row_scales: bool = False) -> dict:
     """A random quantized matrix [n][k] (or a stack of `experts` of them).
 
     Returns {fmt, n, k, q, s, z} with numpy arrays laid out as the library's
-    formats define (leading expert dimension when experts > 0)."""
+    formats define (leading expert dimension when experts > 0).  INT8 row
+    scales are the constant 1/(127*sqrt(k)) unless row_scales, which draws one
+    per row from U(0.5,1.5)/(127*sqrt(k))."""
     e = max(1, experts)
     lead = (experts,) if experts else ()
     if fmt == FMT_INT8_ROW:
@@ -119,7 +123,11 @@ def qmat(fmt: int, n: int, k: int, key: int, experts: int = 0) -> dict:
         cnt = e * n * k
         raw = stream_u64(tensor_key(key, 1), (cnt + 3) // 4).view(np.uint16)[:cnt]
         q = ((raw.astype(np.int32) % 255) - 127).astype(np.int8).reshape(lead + (n, k))
-        s = np.full(lead + (n,), 1.0 / (127.0 * math.sqrt(k)), dtype=np.float32)
+        if row_scales:
+            s = ((0.5 + uniform(tensor_key(key, 2), e * n)) / (127.0 * math.sqrt(k))).astype(np.float32)
+            s = s.reshape(lead + (n,))
+        else:
+            s = np.full(lead + (n,), 1.0 / (127.0 * math.sqrt(k)), dtype=np.float32)
         return dict(fmt=fmt, n=n, k=k, q=q, s=s, z=None)
     if fmt == FMT_INT4_AFFINE_G64:
         assert k % 64 == 0
@@ -131,12 +139,13 @@ def qmat(fmt: int, n: int, k: int, key: int, experts: int = 0) -> dict:
     raise ValueError(f"unknown format {fmt}")
 
 
-def ffn(fmt_gu: int, fmt_down: int, hidden: int, inter: int, key: int, experts: int = 0) -> dict:
+def ffn(fmt_gu: int, fmt_down: int, hidden: int, inter: int, key: int, experts: int = 0,
+        row_scales: bool = False) -> dict:
     """gate/up [inter][hidden] and down [hidden][inter]."""
     return dict(
-        gate=qmat(fmt_gu, inter, hidden, tensor_key(key, 11), experts),
-        up=qmat(fmt_gu, inter, hidden, tensor_key(key, 12), experts),
-        down=qmat(fmt_down, hidden, inter, tensor_key(key, 13), experts),
+        gate=qmat(fmt_gu, inter, hidden, tensor_key(key, 11), experts, row_scales),
+        up=qmat(fmt_gu, inter, hidden, tensor_key(key, 12), experts, row_scales),
+        down=qmat(fmt_down, hidden, inter, tensor_key(key, 13), experts, row_scales),
     )
 
 
@@ -184,10 +193,12 @@ CONFIGS = {
 }
 
 
-def dense_inputs(hidden: int, inter: int, m: int, fmt: int, seed: int, fmt_down: int | None = None) -> dict:
-    """Weights, x and residual of one dense FFN layer."""
+def dense_inputs(hidden: int, inter: int, m: int, fmt: int, seed: int, fmt_down: int | None = None,
+                 row_scales: bool = False) -> dict:
+    """Weights, x and residual of one dense FFN layer (row_scales: see qmat)."""
     return dict(
-        ffn=ffn(fmt, fmt if fmt_down is None else fmt_down, hidden, inter, tensor_key(seed, 100)),
+        ffn=ffn(fmt, fmt if fmt_down is None else fmt_down, hidden, inter, tensor_key(seed, 100),
+                row_scales=row_scales),
         x=act_rows(tensor_key(seed, 101), m, hidden),
         resid=act_rows(tensor_key(seed, 102), m, hidden),
         norm_w=norm_weight(tensor_key(seed, 103), hidden),
@@ -210,11 +221,12 @@ def moe_inputs(hidden: int, n_experts: int, moe_inter: int, m: int, seed: int,
     return d
 
 
-def config_inputs(c: int, m: int) -> dict:
-    """Inputs of workload c at m tokens; the seed of workload c is c."""
+def config_inputs(c: int, m: int, row_scales: bool = False) -> dict:
+    """Inputs of workload c at m tokens; the seed of workload c is c.  row_scales
+    replaces the INT8 workloads' constant row scale by per-row draws (qmat)."""
     cfg = CONFIGS[c]
     if cfg["kind"] in ("dense", "shared"):
-        return dense_inputs(cfg["hidden"], cfg["inter"], m, cfg["fmt"], seed=c)
+        return dense_inputs(cfg["hidden"], cfg["inter"], m, cfg["fmt"], seed=c, row_scales=row_scales)
     return moe_inputs(cfg["hidden"], cfg["n_experts"], cfg["moe_inter"], m, seed=c,
                       shared_inter=cfg["shared_inter"], fmt=cfg["fmt"])
 

@@ -10,6 +10,7 @@ All arrays are host numpy arrays; bf16 values travel as uint16 bit patterns.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 import subprocess
@@ -23,14 +24,22 @@ LIB = os.path.join(HERE, "liboracle.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY = 0, -1, -2, -3
 
 
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str, extra: tuple = ()) -> str:
+    """gcc one oracle source file (oracle.c, or a test's variant of it) into a shared library."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call(["gcc", *CFLAGS, *extra, "-I", HERE, "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (no FMA contraction, IEEE double)."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < max(
             os.path.getmtime(SRC), os.path.getmtime(os.path.join(HERE, "oracle.h"))):
-        tmp = LIB + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-                               "-shared", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB)
+        compile_source(SRC, LIB)
     return LIB
 
 
@@ -42,41 +51,59 @@ class QMat(C.Structure):
 _lib = None
 
 
+def _load(path: str):
+    """Load an oracle build and declare its functions' signatures."""
+    L = C.CDLL(path)
+    vp, i32, f32 = C.c_void_p, C.c_int, C.c_float
+    P = C.POINTER(QMat)
+    sig = {
+        "or_bf16_value": (C.c_double, [C.c_uint16]),
+        "or_bf16_round": (C.c_uint16, [C.c_double]),
+        "or_dequant": (f32, [P, i32, i32]),
+        "or_dequant_matrix": (None, [P, vp]),
+        "or_gemv": (None, [P, vp, vp]),
+        "or_silu": (C.c_double, [C.c_double]),
+        "or_gelu_tanh": (C.c_double, [C.c_double]),
+        "or_act": (f32, [i32, f32, f32]),
+        "or_residual": (C.c_uint16, [C.c_uint16, f32]),
+        "or_rmsnorm_row": (None, [vp, vp, i32, f32, vp]),
+        "or_gate_logit": (f32, [vp, vp, i32]),
+        "or_sigmoid_gate": (C.c_uint16, [f32, f32]),
+        "or_router_logits": (None, [vp, vp, i32, i32, i32, vp]),
+        "or_dense": (i32, [P, P, P, i32, i32, i32, i32, i32, vp, vp, vp, f32]),
+        "or_shared_expert": (i32, [P, P, P, i32, i32, i32, i32, i32, vp, vp, vp, f32]),
+        "or_topk_token": (None, [vp, vp, i32, i32, vp, vp]),
+        "or_moe_plan": (i32, [vp, i32, i32, i32, i32, vp]),
+        "or_moe_route": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp]),
+        "or_seeded_sum": (f32, [f32, vp, vp, i32]),
+        "or_moe_routed": (i32, [P, P, P, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         build()
-        L = C.CDLL(LIB)
-        vp, i32, f32 = C.c_void_p, C.c_int, C.c_float
-        P = C.POINTER(QMat)
-        sig = {
-            "or_bf16_value": (C.c_double, [C.c_uint16]),
-            "or_bf16_round": (C.c_uint16, [C.c_double]),
-            "or_dequant": (f32, [P, i32, i32]),
-            "or_dequant_matrix": (None, [P, vp]),
-            "or_gemv": (None, [P, vp, vp]),
-            "or_silu": (C.c_double, [C.c_double]),
-            "or_gelu_tanh": (C.c_double, [C.c_double]),
-            "or_act": (f32, [i32, f32, f32]),
-            "or_residual": (C.c_uint16, [C.c_uint16, f32]),
-            "or_rmsnorm_row": (None, [vp, vp, i32, f32, vp]),
-            "or_gate_logit": (f32, [vp, vp, i32]),
-            "or_sigmoid_gate": (C.c_uint16, [f32, f32]),
-            "or_router_logits": (None, [vp, vp, i32, i32, i32, vp]),
-            "or_dense": (i32, [P, P, P, i32, i32, i32, i32, i32, vp, vp, vp, f32]),
-            "or_shared_expert": (i32, [P, P, P, i32, i32, i32, i32, i32, vp, vp, vp, f32]),
-            "or_topk_token": (None, [vp, vp, i32, i32, vp, vp]),
-            "or_moe_plan": (i32, [vp, i32, i32, i32, i32, vp]),
-            "or_moe_route": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp]),
-            "or_seeded_sum": (f32, [f32, vp, vp, i32]),
-            "or_moe_routed": (i32, [P, P, P, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
-        }
-        for name, (res, args) in sig.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = _load(LIB)
     return _lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route every oracle call to another build of the oracle's source (a test
+    plants a mistake in a copy of oracle.c this way and checks that a pin fails)."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def _p(a):

@@ -82,6 +82,45 @@ def test_dequant_int8_hand():
     assert not np.any(w[4:])
 
 
+def test_dequant_int8_rows_hand():
+    # three rows with different scales: each row's weights carry its own scale
+    g = golden("dequant_hand.json")["int8_rows"]
+    n = len(g["s"])
+    q = np.zeros((n, g["k"]), np.int8)
+    q[:, :4] = g["q_head"]
+    mat = dict(fmt=gen.FMT_INT8_ROW, n=n, k=g["k"], q=q, s=np.array(g["s"], np.float32), z=None)
+    w = oracle.dequant_matrix(mat)
+    for r in range(n):
+        assert list(w[r, :4]) == g["expect_head"][r], r
+        assert not np.any(w[r, 4:])
+
+
+def test_dequant_int4_rows_hand():
+    # two rows with the same codes and different scale/zero pairs
+    g = golden("dequant_hand.json")["int4_rows"]
+    k, n = g["k"], len(g["s"])
+    q = np.full((n, k // 2), g["byte_default"], np.uint8)
+    for i, b in g["bytes_nondefault"].items():
+        q[:, int(i)] = b
+    mat = dict(fmt=gen.FMT_INT4_AFFINE_G64, n=n, k=k, q=q, s=gen.bf16_bits(np.array(g["s"])),
+               z=gen.bf16_bits(np.array(g["z"])))
+    w = oracle.dequant_matrix(mat)
+    for r in range(n):
+        for col, want in g["expect"][r].items():
+            assert w[r, int(col)] == want, (r, col)
+
+
+def test_gemv_accumulates_beyond_fp32():
+    # O2: the exact dot product 2^24 + 1 - 2^24 = 1 needs more than fp32's 24
+    # bits while it is summed; the oracle sums in double and rounds once
+    q = np.zeros((1, 64), np.int8)
+    q[0, :3] = [64, 1, -64]
+    mat = dict(fmt=gen.FMT_INT8_ROW, n=1, k=64, q=q, s=np.array([1.0], np.float32), z=None)
+    x = np.zeros(64)
+    x[:3] = [2.0 ** 18, 1.0, 2.0 ** 18]
+    assert oracle.gemv(mat, x)[0] == 1.0
+
+
 # ---------------------------------------------------------------------------
 # O3 activations
 
@@ -150,6 +189,9 @@ def test_residual_single_rounding():
     assert oracle.residual(one, 2.0 ** -8 + 2.0 ** -20) == 0x3F81    # above the tie
     assert oracle.residual(one, 3 * 2.0 ** -8) == 0x3F82             # tie -> even (up)
     assert oracle.residual(0xC000, 2.0) == 0x0000                    # -2 + 2 = +0
+    # 1 + 2^-8 + 2^-30 is just above the tie, but an fp32 sum would drop the
+    # 2^-30 and then round the tie to even: one rounding, from the exact sum
+    assert oracle.residual(one, 2.0 ** -8 + 2.0 ** -30) == 0x3F81
 
 
 def test_sigmoid_gate_closed_forms():
@@ -422,48 +464,54 @@ def test_zero_input():
     assert np.all((out & 0x7FFF) == 0)
 
 
-def integer_regime(fmt, hidden, inter, m, seed):
-    """Inputs on which every partial sum is an exact small integer (P11).
+def integer_regime(fmt, hidden, inter, m, seed, free_col=False):
+    """Inputs on which every partial sum is an exact dyadic number (P11).
     x in {-2..2} with x[:, :4] = 2; the gate's first four columns carry a large
-    weight so that g >= 24, where silu(g) == gelu(g) == g in fp32; |g*u| < 2^16
-    so act is exact as a pair of bf16 halves; power-of-two scales.
+    weight so that g >= 24, where silu(g) == gelu(g) == g in fp32; g*u is a
+    multiple of 1/2 below 2^15, so act is exact as a pair of bf16 halves.  The
+    scales are powers of two drawn per row (INT8) or per (row, group) (INT4):
+    gate 2 or 4, up 1/4 or 1/2, down 2^-9, 2^-10 or 2^-11, so a kernel that
+    applies another row's (or group's) scale loses bit-exactness.
+    free_col: the last input column gets zero gate/up weights, so x[:, -1] may
+    hold anything without changing h (the sigmoid-gate pin puts the logit there).
     Returns (ffn, x_bits, resid_bits, exact h [m][hidden], resid ints)."""
     rng = np.random.default_rng(seed)
     x = rng.integers(-2, 3, (m, hidden))
     x[:, :4] = 2
     sparse = lambda shape: rng.integers(-1, 2, shape) * (rng.random(shape) < 0.25)  # noqa: E731
-    if fmt == gen.FMT_INT8_ROW:
-        qg = sparse((inter, hidden))
-        qg[:, :4] = 8
-        qu = sparse((inter, hidden))
-        qd = sparse((hidden, inter))
-        sg, su, sd = 2.0, 1.0, 2.0 ** -10
+    int8 = fmt == gen.FMT_INT8_ROW
 
-        def mk(q, s):
-            return dict(fmt=fmt, n=q.shape[0], k=q.shape[1], q=q.astype(np.int8),
-                        s=np.full(q.shape[0], s, np.float32), z=None)
-        ffn = dict(gate=mk(qg, sg), up=mk(qu, su), down=mk(qd, sd))
-    else:
-        def mk(w, s):
-            codes = (w + 8).astype(np.uint8)
-            n, k = codes.shape
-            q = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-            return dict(fmt=fmt, n=n, k=k, q=q, s=gen.bf16_bits(np.full((n, k // 64), s)),
-                        z=gen.bf16_bits(np.full((n, k // 64), 8.0)))
-        qg = sparse((inter, hidden))
-        qg[:, :4] = 7
-        qu = sparse((inter, hidden))
-        qd = sparse((hidden, inter))
-        sg, su, sd = 2.0, 1.0, 2.0 ** -10
-        ffn = dict(gate=mk(qg, sg), up=mk(qu, su), down=mk(qd, sd))
-    g = x @ (qg * sg).T.astype(np.float64)
-    u = x @ (qu * su).T.astype(np.float64)
+    def scales(n, k, choices):
+        return rng.choice(np.array(choices, np.float64), size=(n,) if int8 else (n, k // 64))
+
+    def deq(q, s):   # the dequantised weights, exactly (float64)
+        return q * (s[:, None] if int8 else np.repeat(s, 64, axis=1))
+
+    def mk(q, s):
+        n, k = q.shape
+        if int8:
+            return dict(fmt=fmt, n=n, k=k, q=q.astype(np.int8), s=s.astype(np.float32), z=None)
+        codes = (q + 8).astype(np.uint8)
+        packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+        return dict(fmt=fmt, n=n, k=k, q=packed, s=gen.bf16_bits(s), z=gen.bf16_bits(np.full((n, k // 64), 8.0)))
+
+    qg = sparse((inter, hidden))
+    qg[:, :4] = 8 if int8 else 7
+    qu = sparse((inter, hidden))
+    qd = sparse((hidden, inter))
+    if free_col:
+        qg[:, -1] = 0
+        qu[:, -1] = 0
+    sg = scales(inter, hidden, [2.0, 4.0])
+    su = scales(inter, hidden, [0.25, 0.5])
+    sd = scales(hidden, inter, [2.0 ** -9, 2.0 ** -10, 2.0 ** -11])
+    ffn = dict(gate=mk(qg, sg), up=mk(qu, su), down=mk(qd, sd))
+    g = x @ deq(qg, sg).T
+    u = x @ deq(qu, su).T
     assert np.all(g >= 24), "gate bias too small for this hidden"
     a = g * u
-    assert np.all(np.abs(a) < 2 ** 16)
-    hi = a @ qd.T.astype(np.float64)          # integer; h = hi * sd
-    assert np.all(np.abs(hi) < 2 ** 24)
-    h = hi * sd
+    assert np.all(np.abs(a) < 2 ** 15) and np.all(a * 2 == np.round(a * 2))
+    h = a @ deq(qd, sd).T                     # exact in double: multiples of 2^-12, far below 2^53 of them
     resid = rng.integers(-64, 65, (m, hidden))
     return ffn, gen.bf16_bits(x), gen.bf16_bits(resid), h, resid
 
@@ -478,6 +526,109 @@ def test_integer_regime_exact(fmt, act):
     assert np.array_equal(out, want)
     out = oracle.shared_expert(ffn, hidden, inter, act, gen.TAIL_NONE, x, None)
     assert np.array_equal(out, np.vectorize(bf16_rne)(h).astype(np.uint16))
+
+
+def half_bits(b):
+    """bf16 bits of half a bf16 value (exact for normal values)."""
+    return np.vectorize(lambda v: bf16_rne(bf16_val(int(v)) / 2.0))(b).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64])
+def test_shared_expert_zero_gate_halves(fmt):
+    # P10 at m >= 2: a zero gate vector gives sigmoid(0) = 1/2 on every token,
+    # so the gated branch is exactly half the ungated one
+    hidden, inter, m = 256, 384, 5
+    inp = gen.dense_inputs(hidden, inter, m, fmt, seed=90 + fmt, row_scales=True)
+    none = oracle.shared_expert(inp["ffn"], hidden, inter, gen.ACT_GELU_TANH, gen.TAIL_NONE, inp["x"], None)
+    gated = oracle.shared_expert(inp["ffn"], hidden, inter, gen.ACT_GELU_TANH, gen.TAIL_SIGMOID_GATE, inp["x"],
+                                 np.zeros(hidden, np.uint16))
+    assert np.array_equal(gated, half_bits(none))
+
+
+SIG_LOGITS = (0.0, 100.0, -200.0)   # sigmoid: exactly 1/2, 1 and (to bf16) 0
+
+
+def sigmoid_gate_case(fmt, hidden, inter, m, seed):
+    """The integer-regime FFN with the last input column free; x[t][-1] holds
+    token t's logit and the gate vector selects that column, so the logit of
+    token t is exactly SIG_LOGITS[t % 3].  Returns (ffn, x, gate_vec, expected
+    seed bits): bf16(h/2), bf16(h) and a signed zero."""
+    ffn, x, _, h, _ = integer_regime(fmt, hidden, inter, m, seed, free_col=True)
+    x = x.copy()
+    lg = np.array([SIG_LOGITS[t % 3] for t in range(m)])
+    x[:, -1] = gen.bf16_bits(lg)
+    gv = np.zeros(hidden, np.uint16)
+    gv[-1] = gen.bf16_bits(1.0)
+    want = np.empty((m, hidden), np.uint16)
+    for t in range(m):
+        if lg[t] == 0.0:
+            want[t] = [bf16_rne(v / 2.0) for v in h[t]]
+        elif lg[t] > 0:
+            want[t] = [bf16_rne(v) for v in h[t]]
+        else:
+            want[t] = np.where(h[t] < 0, 0x8000, 0x0000)
+    return ffn, x, gv, want
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64])
+def test_sigmoid_gate_composed_per_token(fmt):
+    # each token's logit comes from its own row of x (a logit read from another
+    # token, or a bf16-rounded one, changes the result)
+    ffn, x, gv, want = sigmoid_gate_case(fmt, 128, 192, 5, 95 + fmt)
+    got = oracle.shared_expert(ffn, 128, 192, gen.ACT_SILU, gen.TAIL_SIGMOID_GATE, x, gv)
+    assert np.array_equal(got, want)
+
+
+RMS_G = (24.0, 32.0, 48.0, 64.0, 96.0, 128.0)
+
+
+def rmsnorm_case(fmt, hidden, inter, m, seed):
+    """A selection FFN whose h rows have constant magnitude, h_t[i] = +-G_t, so
+    that rmsnorm(h_t) * w = +-w exactly (mean(h^2) = G_t^2, and eps = 1e-6
+    moves G_t / sqrt(G_t^2 + eps) by under 1e-9, far below half a bf16 ulp).
+    Gate row n selects input 0 (x_t[0] = G_t >= 24, where f(g) = g), up row
+    n < hidden selects input 1 + n % (hidden - 1) (x = +-1 there; rows past
+    hidden are zero), down row i selects act sigma(i) for a permutation sigma.
+    Returns (ffn, x bits, norm weight bits, expected bits)."""
+    rng = np.random.default_rng(seed)
+    sigma = rng.permutation(hidden)
+
+    def mat(n, k, sel):
+        if fmt == gen.FMT_INT8_ROW:
+            q = np.zeros((n, k), np.int8)
+            for r, c in sel:
+                q[r, c] = 1
+            return dict(fmt=fmt, n=n, k=k, q=q, s=np.ones(n, np.float32), z=None)
+        codes = np.full((n, k), 8, np.uint8)
+        for r, c in sel:
+            codes[r, c] = 9
+        return dict(fmt=fmt, n=n, k=k, q=(codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8),
+                    s=gen.bf16_bits(np.ones((n, k // 64))), z=gen.bf16_bits(np.full((n, k // 64), 8.0)))
+
+    ffn = dict(gate=mat(inter, hidden, [(nn, 0) for nn in range(inter)]),
+               up=mat(inter, hidden, [(nn, 1 + nn % (hidden - 1)) for nn in range(hidden)]),
+               down=mat(hidden, inter, [(i, sigma[i]) for i in range(hidden)]))
+    sgn = rng.choice([-1.0, 1.0], size=(m, hidden))
+    x = sgn.copy()
+    x[:, 0] = [RMS_G[t % len(RMS_G)] for t in range(m)]
+    w = gen.norm_weight(seed + 1, hidden)
+    neg = np.array([[x[t, 1 + sigma[i] % (hidden - 1)] < 0 for i in range(hidden)] for t in range(m)])
+    want = np.where(neg, w | 0x8000, w).astype(np.uint16)
+    return ffn, gen.bf16_bits(x), w, want
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64])
+def test_rmsnorm_composed_closed_form(fmt):
+    # the RMSNorm tail of both the dense layer and the shared expert: +-w, with
+    # each token's own sign pattern (a norm over another token's h, over inter
+    # instead of hidden, or of a transposed FFN fails)
+    hidden, inter, m = 128, 192, 4
+    ffn, x, w, want = rmsnorm_case(fmt, hidden, inter, m, 70 + fmt)
+    for act in (gen.ACT_SILU, gen.ACT_GELU_TANH):
+        got = oracle.dense(ffn, hidden, inter, act, gen.TAIL_RMSNORM, x, None, w, 1e-6)
+        assert np.array_equal(got, want)
+        got = oracle.shared_expert(ffn, hidden, inter, act, gen.TAIL_RMSNORM, x, w, 1e-6)
+        assert np.array_equal(got, want)
 
 
 def test_batched_equals_per_token():
