@@ -249,6 +249,9 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
             if (cached) ids_s[t * k + lane] = my_e;
         }
     }
+    // Token t's ids were written by wave t % nw; the plan pass below reads
+    // every pair's id from any thread, so all waves' writes must land first.
+    __syncthreads();
 
     // ---- plan: unused entries are -1 ----
     const int total = 2 * m + 4 + 4 * m * k;

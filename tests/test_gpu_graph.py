@@ -1,14 +1,17 @@
-"""HIP-graph capture of the library's calls: a captured dense call and a
-captured route + routed call are replayed several times, with eager work and
-synchronisation between the replays, and every replay must equal the eager
-result bit for bit (the calls enqueue only kernels: no memset or copy nodes)."""
+"""HIP-graph capture of the library's calls: a captured dense call, a
+captured route + routed call and a captured route + whole MoE layer are
+replayed several times, with eager work and synchronisation between the
+replays; every replay must equal the eager result bit for bit (the calls
+enqueue only kernels: no memset or copy nodes), and the replayed result is
+checked against the CPU oracle."""
 import numpy as np
 import pytest
 import torch
 
 import gen
 import moe_expert_dequant_amd as fq
-from test_gpu_parity import LAYOUTS, dev, dev16, ffn_dev, mats_dev, say
+import oracle
+from test_gpu_parity import LAYOUTS, check, dev, dev16, ffn_dev, host16, mats_dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +39,8 @@ def test_graph_replay_dense(tiled):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(r, want), rep
+    want_o = oracle.dense(inp["ffn"], hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, inp["x"], inp["resid"])
+    check(host16(r), want_o, f"graph dense replay vs oracle tiled {tiled}")
 
 
 @LAYOUTS
@@ -46,7 +51,8 @@ def test_graph_replay_routed(tiled):
     d = mats_dev(inp["experts"], tiled, E)
     st = fq.ffn_struct(d)
     x, r0, lg = dev16(inp["x"]), dev16(inp["resid"]), dev(inp["logits"].astype(np.float32))
-    seed = dev16(gen.act_rows(gen.tensor_key(4344, m), m, hidden))
+    seed_bits = gen.act_rows(gen.tensor_key(4344, m), m, hidden)
+    seed = dev16(seed_bits)
     ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
     w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
     plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
@@ -71,3 +77,52 @@ def test_graph_replay_routed(tiled):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(r, want), rep
+    rc, ids_o, w_o, plan_o = oracle.moe_route(inp["logits"], k, cap)
+    assert rc == 0 and np.array_equal(ids.cpu().numpy(), ids_o) and np.array_equal(plan.cpu().numpy(), plan_o)
+    want_o = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids_o, w_o, seed_bits,
+                               inp["resid"])
+    check(host16(r), want_o, f"graph routed replay vs oracle tiled {tiled}")
+
+
+@LAYOUTS
+def test_graph_replay_moe_layer(tiled):
+    # route + ffnq_moe_layer with a gated shared expert, captured once and
+    # replayed; the replays equal the eager layer and the oracle chain
+    hidden, inter, E, m, k, cap, sh_inter = 512, 256, 32, 4, 8, 32, 384
+    say("graph moe layer", tiled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4545, shared_inter=sh_inter)
+    ex_d = mats_dev(inp["experts"], tiled, E)    # the device tensors stay referenced while they are used
+    ex = fq.ffn_struct(ex_d)
+    sh_d, sh = ffn_dev(inp["shared"], tiled)
+    x, r0, lg, gv = dev16(inp["x"]), dev16(inp["resid"]), dev(inp["logits"].astype(np.float32)), dev16(inp["gate_vec"])
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    ws = fq.Workspace()
+
+    def layer(resid):
+        fq.moe_route(lg, m, E, k, cap, ids, w, plan)
+        fq.moe_layer(ex, E, hidden, inter, m, k, gen.ACT_SILU, sh, sh_inter, gv, x, ids, w, plan, resid, ws=ws)
+
+    want = r0.clone()
+    layer(want)
+    torch.cuda.synchronize()
+    r = r0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(r)
+    for rep in range(4):
+        r.copy_(r0)
+        ids.fill_(-7)
+        plan.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r, want), rep
+    rc, ids_o, w_o, plan_o = oracle.moe_route(inp["logits"], k, cap)
+    assert rc == 0 and np.array_equal(ids.cpu().numpy(), ids_o)
+    seed_o = oracle.shared_expert(inp["shared"], hidden, sh_inter, gen.ACT_SILU, gen.TAIL_SIGMOID_GATE, inp["x"],
+                                  inp["gate_vec"])
+    want_o = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids_o, w_o, seed_o,
+                               inp["resid"])
+    check(host16(r), want_o, f"graph moe layer replay vs oracle tiled {tiled}")

@@ -90,7 +90,7 @@ def ref_pack(mat: dict, n_experts: int) -> np.ndarray:
                                        (gen.FMT_INT8_ROW, 48, 64, 1)])
 def test_pack_layout(fmt, n, k, E):
     print("[case] pack", fmt, n, k, E, flush=True)
-    mat = gen.qmat(fmt, n, k, gen.tensor_key(9000 + n, k), experts=E if E > 1 else 0)
+    mat = gen.qmat(fmt, n, k, gen.tensor_key(9000 + n, k), experts=E if E > 1 else 0, row_scales=True)
     eb = fq.packed_bytes(fmt, n, k)
     want = ref_pack(mat, E)
     assert eb * E == want.size

@@ -2,7 +2,9 @@
 same seeded inputs.  Routes and plans must match bit for bit; bf16 outputs
 must be within a per-row relative L2 error of 2e-3; in the integer-exact
 regime the outputs must match bit for bit."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import gen
 import moe_expert_dequant_amd as fq
 import oracle
 from helpers import rel_l2_rows
-from test_oracle_pins import integer_regime
+from test_oracle_pins import integer_regime, rmsnorm_case, sigmoid_gate_case
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -22,6 +24,33 @@ I8, I4 = gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64
 def say(*a):
     print("[case]", *a, flush=True)
     sys.stdout.flush()
+
+
+# The oracle computes each token on its own, so large cases run it on chunks of
+# tokens in threads (ctypes releases the GIL during the call) and concatenate.
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_by_rows(fn, m, *row_args, **kw):
+    """fn(*chunked row_args, **kw) over token chunks; row_args are [m][...] arrays (or None)."""
+    nch = min(m, ORACLE_THREADS)
+    bounds = [(m * i // nch, m * (i + 1) // nch) for i in range(nch)]
+    def one(b):
+        a, e = b
+        return fn(*[None if r is None else r[a:e] for r in row_args], **kw)
+    with ThreadPoolExecutor(nch) as ex:
+        parts = list(ex.map(one, bounds))
+    return np.concatenate(parts, axis=0)
+
+
+_ORACLE_CACHE = {}
+
+
+def cached(key, fn):
+    """Oracle results shared by the row-major and tiled runs of a case."""
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = fn()
+    return _ORACLE_CACHE[key]
 
 
 def dev16(a):
@@ -99,7 +128,7 @@ DENSE_CASES = [(fg, fd, act, tail, m)
 def test_dense_small(fg, fd, act, tail, m, tiled):
     hidden, inter = 512, 768
     say("dense_small", fg, fd, act, tail, m, "tiled" if tiled else "rowmajor")
-    inp = gen.dense_inputs(hidden, inter, m, fg, seed=1000 + 10 * fg + fd + 100 * m, fmt_down=fd)
+    inp = gen.dense_inputs(hidden, inter, m, fg, seed=1000 + 10 * fg + fd + 100 * m, fmt_down=fd, row_scales=True)
     aux = inp["norm_w"] if tail == gen.TAIL_RMSNORM else None
     want = oracle.dense(inp["ffn"], hidden, inter, act, tail, inp["x"],
                         inp["resid"] if tail == gen.TAIL_RESIDUAL else None, aux)
@@ -113,7 +142,7 @@ def test_dense_small(fg, fd, act, tail, m, tiled):
 def test_shared_expert_small(tail, m, tiled):
     hidden, inter = 384, 640
     say("shared_small", tail, m, tiled)
-    inp = gen.dense_inputs(hidden, inter, m, I8, seed=2000 + m + 7 * tail)
+    inp = gen.dense_inputs(hidden, inter, m, I8, seed=2000 + m + 7 * tail, row_scales=True)
     aux = {gen.TAIL_NONE: None, gen.TAIL_RMSNORM: inp["norm_w"], gen.TAIL_SIGMOID_GATE: inp["gate_vec"]}[tail]
     want = oracle.shared_expert(inp["ffn"], hidden, inter, gen.ACT_GELU_TANH, tail, inp["x"], aux)
     got = gpu_dense(inp, hidden, inter, gen.ACT_GELU_TANH, tail, shared=True, aux=aux, tiled=tiled)
@@ -134,6 +163,51 @@ def test_integer_regime_bit_exact(fmt, act, m, tiled):
     want = oracle.shared_expert(ffn, hidden, inter, act, gen.TAIL_NONE, x, None)
     got = gpu_dense(dict(ffn=ffn, x=x, resid=resid), hidden, inter, act, gen.TAIL_NONE, shared=True, tiled=tiled)
     assert np.array_equal(got, want)
+
+
+@LAYOUTS
+@pytest.mark.parametrize("fmt", [I8, I4])
+def test_sigmoid_gate_composed_bit_exact(fmt, tiled):
+    # per-token logits 0, 100, -200 (from each token's own row of x) on the
+    # integer-exact FFN: bf16(h/2), bf16(h) and +-0, bit for bit
+    hidden, inter, m = 256, 384, 5
+    say("sigmoid_composed", fmt, tiled)
+    ffn, x, gv, want = sigmoid_gate_case(fmt, hidden, inter, m, 500 + fmt)
+    assert np.array_equal(oracle.shared_expert(ffn, hidden, inter, gen.ACT_SILU, gen.TAIL_SIGMOID_GATE, x, gv), want)
+    got = gpu_dense(dict(ffn=ffn, x=x), hidden, inter, gen.ACT_SILU, gen.TAIL_SIGMOID_GATE, shared=True, aux=gv,
+                    tiled=tiled)
+    assert np.array_equal(got, want)
+
+
+@LAYOUTS
+@pytest.mark.parametrize("fmt", [I8, I4])
+@pytest.mark.parametrize("shared", [False, True], ids=["dense", "shared"])
+def test_rmsnorm_composed_bit_exact(fmt, shared, tiled):
+    # a constant-magnitude h per token: rmsnorm(h) * w = +-w with each token's
+    # own sign pattern, bit for bit
+    hidden, inter, m = 256, 384, 6
+    say("rmsnorm_composed", fmt, shared, tiled)
+    ffn, x, w, want = rmsnorm_case(fmt, hidden, inter, m, 600 + fmt)
+    got = gpu_dense(dict(ffn=ffn, x=x), hidden, inter, gen.ACT_GELU_TANH, gen.TAIL_RMSNORM, shared=shared, aux=w,
+                    tiled=tiled)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt,hidden,inter,m", [(I8, 1024, 1536, 2), (I8, 1024, 704, 9), (I4, 1024, 1152, 2),
+                                                (I4, 2048, 1024, 9), (I4, 1024, 1536, 5), (I8, 2048, 704, 11)])
+def test_dense_wide_gate_up(fmt, hidden, inter, m):
+    # tiled dense calls with 2..11 rows take the gate/up shape with runs of two
+    # tiles per workgroup (inter/16 is even whenever inter is a valid down K,
+    # so every run has two tiles); INT8 K of 11 blocks, INT4 of 9 blocks
+    say("dense_wide", fmt, hidden, inter, m)
+    inp = gen.dense_inputs(hidden, inter, m, fmt, seed=5000 + hidden + inter + m, row_scales=True)
+    want = oracle.dense(inp["ffn"], hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, inp["x"], inp["resid"])
+    got = gpu_dense(inp, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, tiled=True)
+    check(got, want, f"dense wide fmt {fmt} {hidden}x{inter} m {m}")
+    zero = dict(inp, resid=np.zeros_like(inp["resid"]))
+    want0 = oracle.dense(inp["ffn"], hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, inp["x"], zero["resid"])
+    check(gpu_dense(zero, hidden, inter, gen.ACT_SILU, gen.TAIL_RESIDUAL, tiled=True), want0,
+          f"dense wide (zero residual) fmt {fmt} {hidden}x{inter} m {m}")
 
 
 @LAYOUTS
@@ -179,7 +253,10 @@ def check_route(logits, k, cap, scale=None, label=""):
                                        (64, 8, 2, 32), (7, 16, 4, 5), (33, 64, 6, 7), (200, 40, 3, 9),
                                        (5, 1024, 32, 32), (3, 3, 3, 3),
                                        # one sub-batch over many pairs (parallel plan), and past the LDS id cache
-                                       (300, 8, 2, 32), (1000, 16, 4, 32), (1100, 16, 4, 32), (64, 128, 8, 32)])
+                                       (300, 8, 2, 32), (1000, 16, 4, 32), (1100, 16, 4, 32), (64, 128, 8, 32),
+                                       # one pair per thread: ids written by several waves, read by all threads
+                                       (2, 16, 4, 32), (4, 16, 8, 32), (8, 16, 8, 32), (8, 64, 4, 32),
+                                       (3, 128, 8, 32), (16, 8, 4, 32), (8, 128, 8, 32)])
 def test_route_random(m, E, k, cap):
     logits = gen.router_logits(gen.tensor_key(m * 1000 + E, k), m, E)
     check_route(logits, k, cap, label="random")
@@ -267,49 +344,117 @@ def test_routed_small(m, k, cap, use_seed, tiled):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads (sampled where the oracle would be slow)
+# prefill-sized routed items (12 or more rows per expert), reduced width, every row
+
+
+@LAYOUTS
+@pytest.mark.parametrize("m,E,k,use_seed", [(64, 8, 2, True), (64, 4, 1, False), (96, 8, 2, False)])
+def test_routed_prefill_sized(m, E, k, use_seed, tiled):
+    hidden, inter, cap = 512, 1024, 32
+    say("routed_prefill", m, E, k, use_seed, tiled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=3500 + m + E + k)
+    seed_bits = gen.act_rows(gen.tensor_key(3600, m), m, hidden) if use_seed else None
+    d = mats_dev(inp["experts"], tiled, E)
+    for resid_kind in ("workload", "zero"):
+        if resid_kind == "zero":
+            inp = dict(inp, resid=np.zeros_like(inp["resid"]))
+        got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, cap, inp, seed_bits)
+        counts = np.bincount(ids.ravel(), minlength=E)
+        assert counts.min() >= 12, counts
+        want = oracle_by_rows(lambda xx, ii, ww, ss, rr: oracle.moe_routed(inp["experts"], E, hidden, inter,
+                                                                          gen.ACT_SILU, xx, ii, ww, ss, rr),
+                              m, inp["x"], ids, w, seed_bits, inp["resid"])
+        check(got, want, f"routed prefill m {m} E {E} k {k} seed {use_seed} resid {resid_kind}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, every row, in the launch configuration bench.py times.
+# "zero" residual variants make the output bf16(h) itself, so the tolerance
+# applies to the FFN output undiluted by the residual stream; "row" scale
+# variants of the INT8 workloads draw a scale per row.
+
+
+def gpu_moe_layer(inp, c, m, tiled, resid):
+    """ffnq_moe_route then ffnq_moe_layer (shared expert, if any, and routed half)."""
+    hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
+    ex = mats_dev(inp["experts"], tiled, E)
+    sh_d, sh = ffn_dev(inp["shared"], tiled) if c["shared_inter"] else (None, None)   # sh_d keeps the tensors
+    ids = torch.full((m, k), -9, dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.full((fq.plan_ints(m, k),), -9, dtype=torch.int32, device="cuda")
+    fq.moe_route(dev(inp["logits"]), m, E, k, c["cap"], ids, w, plan)
+    r = dev16(resid)
+    fq.moe_layer(fq.ffn_struct(ex), E, hidden, inter, m, k, c["act"], sh, c["shared_inter"],
+                 dev16(inp["gate_vec"]) if sh is not None else None, dev16(inp["x"]), ids, w, plan, r)
+    torch.cuda.synchronize()
+    return host16(r), ids.cpu().numpy(), w.cpu().numpy(), plan.cpu().numpy()
+
+
+def oracle_moe_layer(inp, c, m, resid):
+    """The oracle chain: route, gated shared expert (the seed), seeded routed half."""
+    hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
+    rc, ids, w, plan = oracle.moe_route(inp["logits"], k, c["cap"])
+    assert rc == 0
+    seed = None
+    if c["shared_inter"]:
+        seed = oracle_by_rows(lambda xx: oracle.shared_expert(inp["shared"], hidden, c["shared_inter"], c["act"],
+                                                              gen.TAIL_SIGMOID_GATE, xx, inp["gate_vec"]),
+                              m, inp["x"])
+    out = oracle_by_rows(lambda xx, ii, ww, ss, rr: oracle.moe_routed(inp["experts"], E, hidden, inter, c["act"], xx,
+                                                                     ii, ww, ss, rr),
+                         m, inp["x"], ids, w, seed, resid)
+    return ids, w, plan, seed, out
 
 
 @LAYOUTS
 @pytest.mark.parametrize("m", [1, 4])
-def test_config0_dense_int8(m, tiled):
+@pytest.mark.parametrize("scales", ["workload", "row"])
+def test_config0_dense_int8(m, scales, tiled):
     c = gen.CONFIGS[0]
-    say("config0", m, tiled)
-    inp = gen.config_inputs(0, m)
+    say("config0", m, scales, tiled)
+    inp = gen.config_inputs(0, m, row_scales=scales == "row")
     want = oracle.dense(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"], inp["resid"])
     got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], tiled=tiled)
-    check(got, want, f"config0 m {m} tiled {tiled}")
+    check(got, want, f"config0 m {m} scales {scales} tiled {tiled}")
 
 
 @LAYOUTS
 @pytest.mark.parametrize("m", [1, 4])
-def test_config1_llama_int4(m, tiled):
+@pytest.mark.parametrize("resid_kind", ["workload", "zero"])
+def test_config1_llama_int4(m, resid_kind, tiled):
     c = gen.CONFIGS[1]
-    say("config1", m, tiled)
+    say("config1", m, resid_kind, tiled)
     inp = gen.config_inputs(1, m)
+    if resid_kind == "zero":
+        inp["resid"] = np.zeros_like(inp["resid"])
     got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], tiled=tiled)
-    want = oracle.dense(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"], inp["resid"])
-    check(got, want, f"config1 m {m}")
+    want = cached(("c1", m, resid_kind), lambda: oracle_by_rows(
+        lambda xx, rr: oracle.dense(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], xx, rr),
+        m, inp["x"], inp["resid"]))
+    check(got, want, f"config1 m {m} resid {resid_kind}")
 
 
 @LAYOUTS
 @pytest.mark.parametrize("m", [1, 8])
-def test_config2_gemma_shared(m, tiled):
+@pytest.mark.parametrize("scales", ["workload", "row"])
+def test_config2_gemma_shared(m, scales, tiled):
     c = gen.CONFIGS[2]
-    say("config2", m, tiled)
-    inp = gen.config_inputs(2, m)
+    say("config2", m, scales, tiled)
+    inp = gen.config_inputs(2, m, row_scales=scales == "row")
     got = gpu_dense(inp, c["hidden"], c["inter"], c["act"], c["tail"], shared=True, aux=inp["norm_w"], tiled=tiled)
-    rows = list(range(m)) if m <= 2 else [0, m // 2, m - 1]
-    want = oracle.shared_expert(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"][rows],
-                                inp["norm_w"], c["eps"])
-    check(got[rows], want, f"config2 m {m}")
+    want = cached(("c2", m, scales), lambda: oracle_by_rows(
+        lambda xx: oracle.shared_expert(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], xx, inp["norm_w"],
+                                        c["eps"]), m, inp["x"]))
+    check(got, want, f"config2 m {m} scales {scales}")
 
 
 @LAYOUTS
 @pytest.mark.parametrize("m", [1, 2, 4])
-def test_config3_qwen_moe(m, tiled):
+def test_config3_qwen_two_calls(m, tiled):
+    # ffnq_shared_expert (sigmoid-gate tail) against the oracle, then
+    # ffnq_moe_routed_batched on that seed against the oracle on the same seed
     c = gen.CONFIGS[3]
-    say("config3", m, tiled)
+    say("config3 two calls", m, tiled)
     inp = gen.config_inputs(3, m)
     hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
     sh_d, sh_st = ffn_dev(inp["shared"], tiled)
@@ -318,30 +463,50 @@ def test_config3_qwen_moe(m, tiled):
                      dev16(inp["gate_vec"]))
     torch.cuda.synchronize()
     seed_bits = host16(seed)
-    want_seed = oracle.shared_expert(inp["shared"], hidden, c["shared_inter"], c["act"], gen.TAIL_SIGMOID_GATE,
-                                     inp["x"], inp["gate_vec"])
+    want_seed = cached(("c3 seed", m), lambda: oracle.shared_expert(inp["shared"], hidden, c["shared_inter"], c["act"],
+                                                                    gen.TAIL_SIGMOID_GATE, inp["x"], inp["gate_vec"]))
     check(seed_bits, want_seed, f"config3 shared m {m}")
     d = mats_dev(inp["experts"], tiled, E)
     got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, c["cap"], inp, seed_bits)
-    # the routed half is checked on the GPU's own seed, so its error is the routed half's alone
     want = oracle.moe_routed(inp["experts"], E, hidden, inter, c["act"], inp["x"], ids, w, seed_bits, inp["resid"])
     check(got, want, f"config3 routed m {m}")
-    rc, ids_o, w_o, plan_o = oracle.moe_route(inp["logits"], k, c["cap"])
+
+
+@LAYOUTS
+@pytest.mark.parametrize("m", [1, 2, 4])
+@pytest.mark.parametrize("resid_kind", ["workload", "zero"])
+def test_config3_qwen_layer_end_to_end(m, resid_kind, tiled):
+    # ffnq_moe_route + ffnq_moe_layer (the calls bench.py times) against the
+    # oracle chain route -> gated shared expert -> seeded routed half, all on
+    # the oracle's own routes, weights and seed
+    c = gen.CONFIGS[3]
+    say("config3 layer", m, resid_kind, tiled)
+    inp = gen.config_inputs(3, m)
+    if resid_kind == "zero":
+        inp["resid"] = np.zeros_like(inp["resid"])
+    ids_o, w_o, plan_o, _, want = cached(("c3 layer", m, resid_kind),
+                                         lambda: oracle_moe_layer(inp, c, m, inp["resid"]))
+    got, ids, w, plan = gpu_moe_layer(inp, c, m, tiled, inp["resid"])
     assert np.array_equal(ids, ids_o)
+    assert np.array_equal(plan, plan_o)
+    np.testing.assert_allclose(w, w_o, rtol=1e-6, atol=1e-30)
+    check(got, want, f"config3 layer m {m} resid {resid_kind}")
 
 
 @LAYOUTS
 @pytest.mark.parametrize("m", [1, 64])
-def test_config4_mixtral_moe(m, tiled):
+@pytest.mark.parametrize("resid_kind", ["workload", "zero"])
+def test_config4_mixtral_moe(m, resid_kind, tiled):
     c = gen.CONFIGS[4]
-    say("config4", m, tiled)
+    say("config4", m, resid_kind, tiled)
     inp = gen.config_inputs(4, m)
-    hidden, E, inter, k = c["hidden"], c["n_experts"], c["moe_inter"], c["top_k"]
-    d = mats_dev(inp["experts"], tiled, E)
-    got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, c["cap"], inp, None)
-    rows = list(range(m)) if m <= 2 else [0, 21, 42, 63]
-    want = oracle.moe_routed(inp["experts"], E, hidden, inter, c["act"], inp["x"][rows], ids[rows], w[rows], None,
-                             inp["resid"][rows])
-    check(got[rows], want, f"config4 m {m}")
-    counts = np.bincount(ids.ravel(), minlength=E)
+    if resid_kind == "zero":
+        inp["resid"] = np.zeros_like(inp["resid"])
+    ids_o, w_o, plan_o, _, want = cached(("c4", m, resid_kind), lambda: oracle_moe_layer(inp, c, m, inp["resid"]))
+    got, ids, w, plan = gpu_moe_layer(inp, c, m, tiled, inp["resid"])
+    assert np.array_equal(ids, ids_o)
+    assert np.array_equal(plan, plan_o)
+    np.testing.assert_allclose(w, w_o, rtol=1e-6, atol=1e-30)
+    check(got, want, f"config4 m {m} resid {resid_kind}")
+    counts = np.bincount(ids.ravel(), minlength=c["n_experts"])
     say(f"config4 m {m} tokens per expert min {counts.min()} max {counts.max()}")

@@ -466,9 +466,10 @@ def test_zero_input():
 
 def integer_regime(fmt, hidden, inter, m, seed, free_col=False):
     """Inputs on which every partial sum is an exact dyadic number (P11).
-    x in {-2..2} with x[:, :4] = 2; the gate's first four columns carry a large
+    x in {-2..2} with x[:, :8] = 2; the gate's first eight columns carry a large
     weight so that g >= 24, where silu(g) == gelu(g) == g in fp32; g*u is a
-    multiple of 1/2 below 2^15, so act is exact as a pair of bf16 halves.  The
+    multiple of 1/4 below 2^13, so act is exact as a pair of bf16 halves (and
+    the down projection's partial sums stay exact in fp32).  The
     scales are powers of two drawn per row (INT8) or per (row, group) (INT4):
     gate 2 or 4, up 1/4 or 1/2, down 2^-9, 2^-10 or 2^-11, so a kernel that
     applies another row's (or group's) scale loses bit-exactness.
@@ -477,7 +478,7 @@ def integer_regime(fmt, hidden, inter, m, seed, free_col=False):
     Returns (ffn, x_bits, resid_bits, exact h [m][hidden], resid ints)."""
     rng = np.random.default_rng(seed)
     x = rng.integers(-2, 3, (m, hidden))
-    x[:, :4] = 2
+    x[:, :8] = 2
     sparse = lambda shape: rng.integers(-1, 2, shape) * (rng.random(shape) < 0.25)  # noqa: E731
     int8 = fmt == gen.FMT_INT8_ROW
 
@@ -496,13 +497,13 @@ def integer_regime(fmt, hidden, inter, m, seed, free_col=False):
         return dict(fmt=fmt, n=n, k=k, q=packed, s=gen.bf16_bits(s), z=gen.bf16_bits(np.full((n, k // 64), 8.0)))
 
     qg = sparse((inter, hidden))
-    qg[:, :4] = 8 if int8 else 7
+    qg[:, :8] = 8 if int8 else 7
     qu = sparse((inter, hidden))
     qd = sparse((hidden, inter))
     if free_col:
         qg[:, -1] = 0
         qu[:, -1] = 0
-    sg = scales(inter, hidden, [2.0, 4.0])
+    sg = scales(inter, hidden, [1.0, 2.0])
     su = scales(inter, hidden, [0.25, 0.5])
     sd = scales(hidden, inter, [2.0 ** -9, 2.0 ** -10, 2.0 ** -11])
     ffn = dict(gate=mk(qg, sg), up=mk(qu, su), down=mk(qd, sd))
@@ -510,7 +511,7 @@ def integer_regime(fmt, hidden, inter, m, seed, free_col=False):
     u = x @ deq(qu, su).T
     assert np.all(g >= 24), "gate bias too small for this hidden"
     a = g * u
-    assert np.all(np.abs(a) < 2 ** 15) and np.all(a * 2 == np.round(a * 2))
+    assert np.all(np.abs(a) < 2 ** 13) and np.all(a * 4 == np.round(a * 4))
     h = a @ deq(qd, sd).T                     # exact in double: multiples of 2^-12, far below 2^53 of them
     resid = rng.integers(-64, 65, (m, hidden))
     return ffn, gen.bf16_bits(x), gen.bf16_bits(resid), h, resid
