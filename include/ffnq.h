@@ -20,9 +20,10 @@
  *   - Every device pointer must be 16-byte aligned (128-bit loads).  Tensors are
  *     contiguous and row-major, with no strides.
  *   - Ownership: the caller allocates every buffer.  The library allocates,
- *     frees and synchronises nothing and keeps no state between calls (the
- *     one exception, ffnq_set_phase_events, is a per-thread timing switch
- *     that never changes a result).  Calls
+ *     frees and synchronises nothing and keeps no state between calls (two
+ *     exceptions: ffnq_set_phase_events, a per-thread timing switch that never
+ *     changes a result, and the per-GPU scratch array of ffnq_dense_noalloc,
+ *     a static device array rather than an allocation).  Calls
  *     are asynchronous on `stream`; the caller keeps every buffer alive (and
  *     unmodified, for inputs) until the stream's work has completed -- the ABI
  *     form of the pages' rule that weight memory must outlive in-flight work
@@ -170,6 +171,27 @@ typedef struct ffnq_ffn {
 FFNQ_API int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
                const uint16_t* x, uint16_t* out, const uint16_t* norm_w, float eps,
                void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* ---- ffnq_dense_noalloc ------------------------------------------------------
+ * ffnq_dense for callers that cannot allocate device memory (code recorded into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without (ws, ws_bytes), the same kernels and bit-identical results.
+ * Its workspace is a device array inside the library, FFNQ_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call allocates and frees nothing.  Every call on one GPU uses that GPU's
+ * array, so calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller; a later call may start as soon as the
+ * earlier one's kernels have completed on the stream (the array's contents on
+ * entry do not matter).
+ * Errors: those of ffnq_dense; FFNQ_ERR_WORKSPACE when the call needs more than
+ * FFNQ_NOALLOC_SCRATCH_BYTES (the same query ffnq_dense answers with ws == NULL
+ * gives the size; nothing is enqueued); FFNQ_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+#define FFNQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+FFNQ_API int ffnq_dense_noalloc(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail,
+                                const uint16_t* x, uint16_t* out, const uint16_t* norm_w, float eps,
+                                hipStream_t stream);
 
 /* ---- ffnq_shared_expert ----------------------------------------------------
  * The shared (dense) expert branch: the same gated FFN with the shared

@@ -29,7 +29,8 @@ TAIL_SIGMOID_GATE = 3
 
 OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
-EXPORTS = ("ffnq_dense", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route", "ffnq_moe_routed_batched",
+EXPORTS = ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
+           "ffnq_moe_routed_batched",
            "ffnq_moe_layer",
            "ffnq_status_string", "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
 
@@ -68,11 +69,13 @@ def lib():
         FP = C.POINTER(Ffn)
         L.ffnq_dense.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
         L.ffnq_shared_expert.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp, sz, vp]
+        L.ffnq_dense_noalloc.argtypes = [FP, i32, i32, i32, i32, i32, vp, vp, vp, f32, vp]
         L.ffnq_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.ffnq_moe_route.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
         L.ffnq_moe_routed_batched.argtypes = [FP, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ffnq_moe_layer.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("ffnq_dense", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route", "ffnq_moe_routed_batched",
+        for f in ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
+                  "ffnq_moe_routed_batched",
                   "ffnq_moe_layer"):
             getattr(L, f).restype = C.c_int
         L.ffnq_status_string.argtypes = [C.c_int]
@@ -177,6 +180,16 @@ def dense(ffn: Ffn, hidden: int, inter: int, m: int, act: int, tail: int, x, out
     args = (C.byref(ffn), hidden, inter, m, act, tail, _ptr(x), _ptr(out), _ptr(norm_w), eps)
     buf, n = _ws(L.ffnq_dense, args, ws)
     _check("ffnq_dense", L.ffnq_dense(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # FFNQ_NOALLOC_SCRATCH_BYTES
+
+
+def dense_noalloc(ffn: Ffn, hidden: int, inter: int, m: int, act: int, tail: int, x, out, norm_w=None,
+                  eps: float = 1e-6, stream=None):
+    """ffnq_dense_noalloc: ffnq_dense on the library's own per-GPU scratch array (no workspace argument)."""
+    _check("ffnq_dense_noalloc", lib().ffnq_dense_noalloc(C.byref(ffn), hidden, inter, m, act, tail, _ptr(x),
+                                                          _ptr(out), _ptr(norm_w), eps, _stream(stream)))
 
 
 def shared_expert(ffn: Ffn, hidden: int, inter: int, m: int, act: int, tail: int, x, h_out, aux=None,

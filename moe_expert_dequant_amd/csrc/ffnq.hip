@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ffnq.h"
 #include "device.h"
@@ -827,6 +828,35 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     return FFNQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free dense call (ffnq_dense_noalloc) keeps its workspace in
+// this file-scope device array: every GPU the library runs on holds one copy,
+// for the life of the process.  Host code never passes the array's name to a
+// kernel (on the host it is a stand-in, not a device address); it asks the
+// runtime once per device for that device's address and uses only that.
+__device__ __align__(256) unsigned char scratch[FFNQ_NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call made with that device current and kept; nullptr if the lookup
+// fails (the caller then returns FFNQ_ERR_HIP).
+void* scratch_address()
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<void*> addr[kMaxDev];
+    static std::mutex mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    addr[dev].store(q, std::memory_order_release);
+    return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -896,6 +926,20 @@ int ffnq_dense(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int t
                const uint16_t* norm_w, float eps, void* ws, size_t* ws_bytes, hipStream_t stream)
 {
     return dense_common(ffn, hidden, inter, m, act, tail, x, out, norm_w, eps, ws, ws_bytes, stream, false);
+}
+
+int ffnq_dense_noalloc(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail, const uint16_t* x,
+                       uint16_t* out, const uint16_t* norm_w, float eps, hipStream_t stream)
+{
+    // the checks and the size query of ffnq_dense; then its launches on the device's scratch array
+    size_t need = 0;
+    const int rc = dense_common(ffn, hidden, inter, m, act, tail, x, out, norm_w, eps, nullptr, &need, stream, false);
+    if (rc != FFNQ_OK) return rc;
+    if (need > (size_t)FFNQ_NOALLOC_SCRATCH_BYTES) return FFNQ_ERR_WORKSPACE;
+    if (m == 0) return FFNQ_OK;
+    void* ws = scratch_address();
+    if (!ws) return FFNQ_ERR_HIP;
+    return dense_common(ffn, hidden, inter, m, act, tail, x, out, norm_w, eps, ws, &need, stream, false);
 }
 
 int ffnq_shared_expert(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail, const uint16_t* x,
