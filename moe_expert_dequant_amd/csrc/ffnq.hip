@@ -15,6 +15,7 @@
 #include "device.h"
 #include "qgemm.h"
 #include "route.h"
+#include "stream.h"
 #include "tail.h"
 #include "tiled.h"
 
@@ -433,17 +434,108 @@ int down_ranges(int fmt, int K, int N, int rows_total, bool dense, int rows_item
 }
 
 // ---------------------------------------------------------------------------
+// burst kernels (stream.h): dense gate/up at 1..4 tokens and dense down at 1..2
+// tokens on tiled weights, for ffnq_dense.  A wave takes `upw` K units of one
+// tile and a workgroup the ks waves that cover the tile's K range.
+
+#ifndef FFNQ_BURST
+#define FFNQ_BURST 1
+#endif
+#ifndef FFNQ_BURST_DN_UPW
+#define FFNQ_BURST_DN_UPW 1
+#endif
+
+struct BurstCfg {
+    bool ok;
+    int upw, ks, R;
+    size_t lds;
+};
+
+BurstCfg burst_cfg(int fmt, int K, int N, int nmat, int R, int upw_pref)
+{
+    BurstCfg c{false, 1, 1, R, 0};
+    if (!FFNQ_BURST || !is_tiled(fmt) || R < 1 || R > 4) return c;
+    const int F = to_fmt(fmt);
+    const TileGeo geo = tile_geo(F, N, K);
+    const int nun = is_int4(fmt) ? geo.ng : (geo.nbk + 7) / 8;
+    c.upw = std::max(1, std::min(upw_pref, nun));
+    c.ks = (nun + c.upw - 1) / c.upw;
+    if (c.ks > 16) {
+        c.upw = 2;
+        c.ks = (nun + 1) / 2;
+    }
+    if (c.ks > 16) return c;
+    c.lds = (size_t)burst_lds(F, nmat, R, c.upw, c.ks);
+    c.ok = c.lds <= kLdsBudget;
+    return c;
+}
+
+BurstCfg dense_gu_burst(const ffnq_ffn* ffn, int hidden, int inter, int m, bool shared)
+{
+    if (shared) return BurstCfg{false, 1, 1, m, 0};
+    BurstCfg c = burst_cfg(ffn->gate.fmt, hidden, inter, 2, m, 1);
+    c.ok = c.ok && c.upw == 1;   // the gate/up burst kernel takes one K unit per wave
+    return c;
+}
+
+BurstCfg dense_down_burst(int fmt_down, int hidden, int inter, int m, bool shared)
+{
+    if (shared || m > 2) return BurstCfg{false, 1, 1, 2 * m, 0};
+    return burst_cfg(fmt_down, inter, hidden, 1, 2 * m, FFNQ_BURST_DN_UPW);
+}
+
+#define FFNQ_GUB_CASE(F, R_)                                                                                   \
+    if (F_ == F && c.R == R_) {                                                                                \
+        hipExtLaunchKernelGGL((gu_burst_kernel<F, R_>), dim3(T), dim3(64 * c.ks), c.lds, stream, phase_event(0), \
+                              phase_event(1), 0, q);                                                           \
+        return true;                                                                                           \
+    }
+
+bool launch_gu_burst(int fmt, const BurstCfg& c, int N, hipStream_t stream, const GUParams& prm)
+{
+    GUParams q = prm;
+    q.ks = c.ks;
+    q.upw = c.upw;
+    const int F_ = to_fmt(fmt);
+    const int T = (N + 15) / 16;
+    FFNQ_GUB_CASE(FMT_INT4, 1) FFNQ_GUB_CASE(FMT_INT4, 2) FFNQ_GUB_CASE(FMT_INT4, 3) FFNQ_GUB_CASE(FMT_INT4, 4)
+    FFNQ_GUB_CASE(FMT_INT8, 1) FFNQ_GUB_CASE(FMT_INT8, 2) FFNQ_GUB_CASE(FMT_INT8, 3) FFNQ_GUB_CASE(FMT_INT8, 4)
+    return false;
+}
+
+#define FFNQ_DNB_CASE(F, R_)                                                                                     \
+    if (F_ == F && c.R == R_) {                                                                                  \
+        hipExtLaunchKernelGGL((down_burst_kernel<F, R_>), dim3(T), dim3(64 * c.ks), c.lds, stream, phase_event(2), \
+                              phase_event(3), 0, q);                                                             \
+        return true;                                                                                             \
+    }
+
+bool launch_down_burst(int fmt, const BurstCfg& c, int N, hipStream_t stream, const DownParams& prm)
+{
+    DownParams q = prm;
+    q.ks = c.ks;
+    q.upw = c.upw;
+    q.KG = 1;
+    const int F_ = to_fmt(fmt);
+    const int T = (N + 15) / 16;
+    FFNQ_DNB_CASE(FMT_INT4, 2) FFNQ_DNB_CASE(FMT_INT4, 4) FFNQ_DNB_CASE(FMT_INT8, 2) FFNQ_DNB_CASE(FMT_INT8, 4)
+    return false;
+}
+
+// ---------------------------------------------------------------------------
 // dense FFN (ffnq_dense and ffnq_shared_expert)
 
 struct DenseWs {
     size_t act, part, logit, total;
 };
 
-DenseWs dense_ws(int fmt_down, int hidden, int inter, int m, int tail)
+DenseWs dense_ws(int fmt_down, int hidden, int inter, int m, int tail, bool shared)
 {
     DenseWs w{};
     size_t o = 0;
-    const int kg = down_ranges(fmt_down, inter, hidden, m, true, m, tail == TAIL_RMSNORM);
+    const int kg = dense_down_burst(fmt_down, hidden, inter, m, shared).ok
+                       ? 1
+                       : down_ranges(fmt_down, inter, hidden, m, true, m, tail == TAIL_RMSNORM);
     w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * m * hidden * sizeof(float), 256);
     w.logit = o; o += align_up((size_t)m * sizeof(float), 256);
@@ -540,7 +632,7 @@ int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, in
 {
     const int cus = device_cus();
     unsigned char* base = static_cast<unsigned char*>(ws);
-    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail);
+    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail, shared);
     const int gfmt = to_fmt(ffn->gate.fmt), dfmt = to_fmt(ffn->down.fmt);
     const bool tiled = is_tiled(ffn->gate.fmt);
 
@@ -548,8 +640,12 @@ int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, in
     const bool sg = tail == FFNQ_TAIL_SIGMOID_GATE;
     const GUParams gp = dense_gu_params(ffn, hidden, inter, m, act, x, gc, reinterpret_cast<uint16_t*>(base + L.act),
                                         sg ? aux : nullptr, sg ? reinterpret_cast<float*>(base + L.logit) : nullptr);
-    if (!(tiled ? launch_gu_tiled(gfmt, gc, stream, gp) : launch_gu(gfmt, gc, 1, inter, stream, gp)))
+    const BurstCfg gb = dense_gu_burst(ffn, hidden, inter, m, shared);
+    if (gb.ok) {
+        if (!launch_gu_burst(ffn->gate.fmt, gb, inter, stream, gp)) return FFNQ_ERR_UNSUPPORTED;
+    } else if (!(tiled ? launch_gu_tiled(gfmt, gc, stream, gp) : launch_gu(gfmt, gc, 1, inter, stream, gp))) {
         return FFNQ_ERR_UNSUPPORTED;
+    }
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     const KConfig dc = dense_down_config(ffn, hidden, inter, m, cus, tail);
@@ -560,22 +656,28 @@ int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, in
         case FFNQ_TAIL_SIGMOID_GATE: dtail = TAIL_SIGMOID; break;
         default: break;
     }
-    const DownParams dp = dense_down_params(ffn, hidden, inter, m, dc, gp.act_out, out,
-                                            reinterpret_cast<float*>(base + L.part),
-                                            reinterpret_cast<const float*>(base + L.logit), dtail);
-    if (!(tiled ? launch_down_tiled(dfmt, dc, stream, dp) : launch_down(dfmt, dc, 1, hidden, stream, dp)))
+    DownParams dp = dense_down_params(ffn, hidden, inter, m, dc, gp.act_out, out,
+                                      reinterpret_cast<float*>(base + L.part),
+                                      reinterpret_cast<const float*>(base + L.logit), dtail);
+    const BurstCfg db = dense_down_burst(ffn->down.fmt, hidden, inter, m, shared);
+    const int kg = db.ok ? 1 : dc.kg;
+    if (db.ok) {
+        dp.KG = 1;
+        if (!launch_down_burst(ffn->down.fmt, db, hidden, stream, dp)) return FFNQ_ERR_UNSUPPORTED;
+    } else if (!(tiled ? launch_down_tiled(dfmt, dc, stream, dp) : launch_down(dfmt, dc, 1, hidden, stream, dp))) {
         return FFNQ_ERR_UNSUPPORTED;
+    }
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
     if (tail == FFNQ_TAIL_RMSNORM) {
         const size_t row_lds = hidden <= kRowLds ? (size_t)hidden * 6 : 0;
-        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(kNormThreads), row_lds, stream, dp.part, dc.kg, m, aux, out, hidden,
+        hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(kNormThreads), row_lds, stream, dp.part, kg, m, aux, out, hidden,
                            eps);
         if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
-    } else if (dc.kg > 1) {
+    } else if (kg > 1) {
         const long long total = (long long)m * hidden;
         const int grid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
-        hipLaunchKernelGGL(ksum_tail_kernel, dim3(grid), dim3(256), 0, stream, dp.part, dc.kg, m, hidden, dp.tail, out,
+        hipLaunchKernelGGL(ksum_tail_kernel, dim3(grid), dim3(256), 0, stream, dp.part, kg, m, hidden, dp.tail, out,
                            dp.logit);
         if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
     }
@@ -605,7 +707,7 @@ int dense_common(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int
         if (!aux || misaligned(aux)) return FFNQ_ERR_INVALID;
     }
     if (tail == FFNQ_TAIL_RMSNORM && !(eps >= 0.0f && std::isfinite(eps))) return FFNQ_ERR_INVALID;
-    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail);
+    const DenseWs L = dense_ws(ffn->down.fmt, hidden, inter, m, tail, shared);
     if (!ws) {
         *ws_bytes = L.total;
         return FFNQ_OK;
@@ -733,7 +835,7 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     GUParams gps{};
     DenseWs Ls{};
     if (sh) {
-        Ls = dense_ws(sh->ffn->down.fmt, hidden, sh->inter, m, FFNQ_TAIL_SIGMOID_GATE);
+        Ls = dense_ws(sh->ffn->down.fmt, hidden, sh->inter, m, FFNQ_TAIL_SIGMOID_GATE, true);
         gcs = dense_gu_config(sh->ffn, hidden, sh->inter, m, cus);
         gps = dense_gu_params(sh->ffn, hidden, sh->inter, m, act, x, gcs,
                               reinterpret_cast<uint16_t*>(sh->base + Ls.act), sh->gate_vec,
@@ -1049,7 +1151,7 @@ int ffnq_moe_layer(const ffnq_ffn* experts, int n_experts, int hidden, int moe_i
     const size_t shared_off = align_up(L.total, 256);
     const size_t total = m == 0 ? 0
                                 : shared_off + (shared ? dense_ws(shared->down.fmt, hidden, shared_inter, m,
-                                                                  FFNQ_TAIL_SIGMOID_GATE).total
+                                                                  FFNQ_TAIL_SIGMOID_GATE, true).total
                                                        : 0);
     if (!ws) {
         *ws_bytes = total;
