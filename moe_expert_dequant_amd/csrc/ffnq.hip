@@ -434,73 +434,84 @@ int down_ranges(int fmt, int K, int N, int rows_total, bool dense, int rows_item
 }
 
 // ---------------------------------------------------------------------------
-// burst kernels (stream.h): dense gate/up at 1..4 tokens and dense down at 1..2
-// tokens on tiled weights, for ffnq_dense.  A wave takes `upw` K units of one
-// tile and a workgroup the ks waves that cover the tile's K range.
+// burst kernels (stream.h): gate/up at 1..4 rows and down at 1..2 tokens on
+// tiled weights.  A workgroup takes one 16-row tile; its ks waves take the
+// tile's K units (gate/up: one each; down: in passes of one).  FFNQ_BURST=0
+// at build time turns them off (the streaming kernels then run every shape).
 
 #ifndef FFNQ_BURST
 #define FFNQ_BURST 1
 #endif
-#ifndef FFNQ_BURST_DN_UPW
-#define FFNQ_BURST_DN_UPW 1
-#endif
 
 struct BurstCfg {
     bool ok;
-    int upw, ks, R;
+    int ks, R;
     size_t lds;
 };
 
-BurstCfg burst_cfg(int fmt, int K, int N, int nmat, int R, int upw_pref)
+// gate/up: one K unit per wave, all of a tile's units in one workgroup.
+BurstCfg burst_gu_cfg(int fmt, int K, int N, int R)
 {
-    BurstCfg c{false, 1, 1, R, 0};
+    BurstCfg c{false, 1, R, 0};
     if (!FFNQ_BURST || !is_tiled(fmt) || R < 1 || R > 4) return c;
     const int F = to_fmt(fmt);
-    const TileGeo geo = tile_geo(F, N, K);
-    const int nun = is_int4(fmt) ? geo.ng : (geo.nbk + 7) / 8;
-    c.upw = std::max(1, std::min(upw_pref, nun));
-    c.ks = (nun + c.upw - 1) / c.upw;
-    if (c.ks > 16) {
-        c.upw = 2;
-        c.ks = (nun + 1) / 2;
-    }
+    c.ks = burst_units(F, N, K);
     if (c.ks > 16) return c;
-    c.lds = (size_t)burst_lds(F, nmat, R, c.upw, c.ks);
+    c.lds = (size_t)burst_lds(F, 2, R, 1, c.ks);
     c.ok = c.lds <= kLdsBudget;
     return c;
 }
 
-BurstCfg dense_gu_burst(const ffnq_ffn* ffn, int hidden, int inter, int m, bool shared)
+// down: up to 16 waves take the tile's K units in passes of one.
+BurstCfg burst_down_cfg(int fmt, int K, int N, int R)
 {
-    if (shared) return BurstCfg{false, 1, 1, m, 0};
-    BurstCfg c = burst_cfg(ffn->gate.fmt, hidden, inter, 2, m, 1);
-    c.ok = c.ok && c.upw == 1;   // the gate/up burst kernel takes one K unit per wave
+    BurstCfg c{false, 1, R, 0};
+    if (!FFNQ_BURST || !is_tiled(fmt) || R < 2 || R > 4) return c;
+    const int F = to_fmt(fmt);
+    const int nu = burst_units(F, N, K);
+    if (nu > 64) return c;
+    c.ks = std::min(nu, 16);
+    c.lds = (size_t)burst_down_lds(F, R, c.ks, nu);
+    c.ok = c.lds <= kLdsBig;
     return c;
 }
 
-BurstCfg dense_down_burst(int fmt_down, int hidden, int inter, int m, bool shared)
+BurstCfg dense_gu_burst(const ffnq_ffn* ffn, int hidden, int inter, int m)
 {
-    if (shared || m > 2) return BurstCfg{false, 1, 1, 2 * m, 0};
-    return burst_cfg(fmt_down, inter, hidden, 1, 2 * m, FFNQ_BURST_DN_UPW);
+    return burst_gu_cfg(ffn->gate.fmt, hidden, inter, m);
 }
 
-#define FFNQ_GUB_CASE(F, R_)                                                                                   \
-    if (F_ == F && c.R == R_) {                                                                                \
-        hipExtLaunchKernelGGL((gu_burst_kernel<F, R_>), dim3(T), dim3(64 * c.ks), c.lds, stream, phase_event(0), \
-                              phase_event(1), 0, q);                                                           \
-        return true;                                                                                           \
+BurstCfg dense_down_burst(int fmt_down, int hidden, int inter, int m)
+{
+    if (m > 2) return BurstCfg{false, 1, 2 * m, 0};
+    return burst_down_cfg(fmt_down, inter, hidden, 2 * m);
+}
+
+#define FFNQ_GUB_CASE(F, R_)                                                                                  \
+    if (F_ == F && R == R_) {                                                                                 \
+        hipExtLaunchKernelGGL((gu_burst_kernel<F, R_>), dim3(na + nb), dim3(64 * ks), lds, stream, phase_event(0), \
+                              phase_event(1), 0, qa, qb, na);                                                 \
+        return true;                                                                                          \
     }
 
-bool launch_gu_burst(int fmt, const BurstCfg& c, int N, hipStream_t stream, const GUParams& prm)
+// One or two gate/up jobs (dense or routed GUParams) in one burst launch: job a
+// on workgroups [0, na), job b (if any) on the next nb; both with R activation
+// rows, ks waves per workgroup (one K unit each) and the same format.
+bool launch_gu_burst_jobs(int fmt, int R, int ks, size_t lds, const GUParams& a, int na, const GUParams* b, int nb,
+                          hipStream_t stream)
 {
-    GUParams q = prm;
-    q.ks = c.ks;
-    q.upw = c.upw;
+    GUParams qa = a, qb = b ? *b : a;
+    qa.ks = qb.ks = ks;
+    if (!b) nb = 0;
     const int F_ = to_fmt(fmt);
-    const int T = (N + 15) / 16;
     FFNQ_GUB_CASE(FMT_INT4, 1) FFNQ_GUB_CASE(FMT_INT4, 2) FFNQ_GUB_CASE(FMT_INT4, 3) FFNQ_GUB_CASE(FMT_INT4, 4)
     FFNQ_GUB_CASE(FMT_INT8, 1) FFNQ_GUB_CASE(FMT_INT8, 2) FFNQ_GUB_CASE(FMT_INT8, 3) FFNQ_GUB_CASE(FMT_INT8, 4)
     return false;
+}
+
+bool launch_gu_burst(int fmt, const BurstCfg& c, int N, hipStream_t stream, const GUParams& prm)
+{
+    return launch_gu_burst_jobs(fmt, c.R, c.ks, c.lds, prm, (N + 15) / 16, nullptr, 0, stream);
 }
 
 #define FFNQ_DNB_CASE(F, R_)                                                                                     \
@@ -514,7 +525,6 @@ bool launch_down_burst(int fmt, const BurstCfg& c, int N, hipStream_t stream, co
 {
     DownParams q = prm;
     q.ks = c.ks;
-    q.upw = c.upw;
     q.KG = 1;
     const int F_ = to_fmt(fmt);
     const int T = (N + 15) / 16;
@@ -533,7 +543,7 @@ DenseWs dense_ws(int fmt_down, int hidden, int inter, int m, int tail, bool shar
 {
     DenseWs w{};
     size_t o = 0;
-    const int kg = dense_down_burst(fmt_down, hidden, inter, m, shared).ok
+    const int kg = dense_down_burst(fmt_down, hidden, inter, m).ok
                        ? 1
                        : down_ranges(fmt_down, inter, hidden, m, true, m, tail == TAIL_RMSNORM);
     w.act = o; o += align_up((size_t)2 * m * inter * 2, 256);
@@ -640,7 +650,7 @@ int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, in
     const bool sg = tail == FFNQ_TAIL_SIGMOID_GATE;
     const GUParams gp = dense_gu_params(ffn, hidden, inter, m, act, x, gc, reinterpret_cast<uint16_t*>(base + L.act),
                                         sg ? aux : nullptr, sg ? reinterpret_cast<float*>(base + L.logit) : nullptr);
-    const BurstCfg gb = dense_gu_burst(ffn, hidden, inter, m, shared);
+    const BurstCfg gb = dense_gu_burst(ffn, hidden, inter, m);
     if (gb.ok) {
         if (!launch_gu_burst(ffn->gate.fmt, gb, inter, stream, gp)) return FFNQ_ERR_UNSUPPORTED;
     } else if (!(tiled ? launch_gu_tiled(gfmt, gc, stream, gp) : launch_gu(gfmt, gc, 1, inter, stream, gp))) {
@@ -659,7 +669,7 @@ int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, in
     DownParams dp = dense_down_params(ffn, hidden, inter, m, dc, gp.act_out, out,
                                       reinterpret_cast<float*>(base + L.part),
                                       reinterpret_cast<const float*>(base + L.logit), dtail);
-    const BurstCfg db = dense_down_burst(ffn->down.fmt, hidden, inter, m, shared);
+    const BurstCfg db = dense_down_burst(ffn->down.fmt, hidden, inter, m);
     const int kg = db.ok ? 1 : dc.kg;
     if (db.ok) {
         dp.KG = 1;
@@ -722,7 +732,7 @@ int dense_common(const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int
 // routed half
 
 struct RoutedWs {
-    size_t act, part, total;
+    size_t act, part, seed, total;
 };
 
 RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k, int n_experts)
@@ -733,6 +743,7 @@ RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k, int n_exper
     size_t o = 0;
     w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
+    w.seed = o; o += align_up((size_t)m * hidden * 2, 256);   // a layer's shared-expert seed
     w.total = m == 0 ? 0 : o;
     return w;
 }
@@ -794,7 +805,80 @@ bool launch_down_tiled2(const KConfig& a, const DownParams& pa, const KConfig& b
     return false;
 }
 
+// The fused routed down (stream.h moe_down_kernel): configuration.  One
+// workgroup per 16-row output tile; its units are the shared expert's K units
+// and those of every possible union entry (at most min(m*k, E)); ks waves take
+// them in passes of one.  For m <= 2 tokens (2m activation rows per unit).
+struct MoeDownCfg {
+    bool ok;
+    int R, ks, max_units;
+    size_t lds;
+};
+
+MoeDownCfg moe_down_cfg(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
+                        const ffnq_ffn* shared, int shared_inter)
+{
+    MoeDownCfg c{false, 2 * m, 1, 0, 0};
+    if (!FFNQ_BURST || m > 2 || !is_tiled(experts->down.fmt) || !is_int4(experts->down.fmt)) return c;
+    int ns = 0;
+    if (shared) {
+        if (!is_tiled(shared->down.fmt) || !is_int4(shared->down.fmt)) return c;
+        if (!dense_down_burst(shared->down.fmt, hidden, shared_inter, m).ok) return c;
+        ns = burst_units(FMT_INT4, hidden, shared_inter);
+    }
+    const int nr = burst_units(FMT_INT4, hidden, moe_inter);
+    const long long umax = std::min<long long>((long long)m * top_k, n_experts);
+    const long long units = ns + umax * nr;
+    if (units > 64) return c;
+    c.max_units = (int)units;
+    c.ks = (int)std::min<long long>(units, 16);
+    c.lds = (size_t)c.ks * burst_wave_lds(FMT_INT4, 1, c.R, 1) + (size_t)c.max_units * 4 * 16 * 4;
+    c.ok = c.lds <= kLdsBig;
+    return c;
+}
+
+#define FFNQ_MDN_CASE(R_)                                                                                      \
+    if (c.R == R_) {                                                                                           \
+        hipExtLaunchKernelGGL((moe_down_kernel<FMT_INT4, R_>), dim3((N + 15) / 16), dim3(64 * c.ks), c.lds, stream, \
+                              phase_event(2), phase_event(3), 0, q);                                           \
+        return true;                                                                                           \
+    }
+
+bool launch_moe_down(const MoeDownCfg& c, int N, hipStream_t stream, const MoeDownParams& prm)
+{
+    MoeDownParams q = prm;
+    q.ks = c.ks;
+    q.max_units = c.max_units;
+    FFNQ_MDN_CASE(2) FFNQ_MDN_CASE(4)
+    return false;
+}
+
+// Gate/up of a layer's shared expert in ffnq_moe_layer: the kernel that
+// ffnq_shared_expert runs for it (burst or streaming), so that its activation,
+// and from it the seed, are bit for bit the same.
+int launch_shared_gu(const LayerShared* sh, int hidden, int m, int act, const uint16_t* x, const GUParams& gps,
+                     const KConfig& gcs, const BurstCfg& sb, hipStream_t stream)
+{
+    if (sb.ok) return launch_gu_burst(sh->ffn->gate.fmt, sb, sh->inter, stream, gps) ? FFNQ_OK : FFNQ_ERR_UNSUPPORTED;
+    const int sfmt = to_fmt(sh->ffn->gate.fmt);
+    (void)hidden;
+    (void)m;
+    (void)act;
+    (void)x;
+    return (is_tiled(sh->ffn->gate.fmt) ? launch_gu_tiled(sfmt, gcs, stream, gps)
+                                        : launch_gu(sfmt, gcs, 1, sh->inter, stream, gps))
+               ? FFNQ_OK
+               : FFNQ_ERR_UNSUPPORTED;
+}
+
 // The routed half on a checked call (m > 0; the routed workspace at base).
+//   m <= 4 and tiled experts: phase 1 is a burst launch (with the shared
+//     expert's gate/up as a second job when their shapes agree);
+//   m <= 2 and tiled INT4 (shared expert too, if any): phase 2, the shared
+//     expert's down, the seeded reduction and the residual add are one launch
+//     (moe_down_kernel);
+//   otherwise the streaming kernels, fp32 per-pair partials and
+//     moe_reduce_kernel.
 int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
                const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
                const uint16_t* seed, uint16_t* resid, unsigned char* base, hipStream_t stream, const LayerShared* sh)
@@ -831,39 +915,104 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
         gp.tebytes = tiled_expert_bytes(experts->gate);
         gp.dfmt = FMT_NATURAL;
     }
+    // the routed gate/up burst: every union entry holds at most m pairs (one per token)
+    const BurstCfg rb = burst_gu_cfg(experts->gate.fmt, hidden, moe_inter, m);
     KConfig gcs{};
     GUParams gps{};
     DenseWs Ls{};
+    BurstCfg sb{};
     if (sh) {
         Ls = dense_ws(sh->ffn->down.fmt, hidden, sh->inter, m, FFNQ_TAIL_SIGMOID_GATE, true);
         gcs = dense_gu_config(sh->ffn, hidden, sh->inter, m, cus);
         gps = dense_gu_params(sh->ffn, hidden, sh->inter, m, act, x, gcs,
                               reinterpret_cast<uint16_t*>(sh->base + Ls.act), sh->gate_vec,
                               reinterpret_cast<float*>(sh->base + Ls.logit));
+        sb = dense_gu_burst(sh->ffn, hidden, sh->inter, m);
     }
-    if (sh && tiled && is_tiled(sh->ffn->gate.fmt) && is_int4(sh->ffn->gate.fmt) &&
-        launch_gu_tiled2(gcs, gps, gc, gp, stream)) {
-        // shared and routed gate/up in one launch
+    const int nr_items = (int)u_est * ((moe_inter + 15) / 16);
+    if (rb.ok) {
+        if (sh && sb.ok && to_fmt(sh->ffn->gate.fmt) == FMT_INT4 && sb.ks == rb.ks && sb.R == rb.R) {
+            // shared and routed gate/up in one burst launch
+            if (!launch_gu_burst_jobs(experts->gate.fmt, rb.R, rb.ks, std::max(sb.lds, rb.lds), gps,
+                                      (sh->inter + 15) / 16, &gp, nr_items, stream))
+                return FFNQ_ERR_UNSUPPORTED;
+        } else {
+            if (sh) {
+                const int rc = launch_shared_gu(sh, hidden, m, act, x, gps, gcs, sb, stream);
+                if (rc != FFNQ_OK) return rc;
+            }
+            if (!launch_gu_burst_jobs(experts->gate.fmt, rb.R, rb.ks, rb.lds, gp, nr_items, nullptr, 0, stream))
+                return FFNQ_ERR_UNSUPPORTED;
+        }
+    } else if (sh && !sb.ok && tiled && is_tiled(sh->ffn->gate.fmt) && is_int4(sh->ffn->gate.fmt) &&
+               launch_gu_tiled2(gcs, gps, gc, gp, stream)) {
+        // shared and routed gate/up in one streaming launch
     } else {
         if (sh) {
-            const int sfmt = to_fmt(sh->ffn->gate.fmt);
-            if (!(is_tiled(sh->ffn->gate.fmt) ? launch_gu_tiled(sfmt, gcs, stream, gps)
-                                              : launch_gu(sfmt, gcs, 1, sh->inter, stream, gps)))
-                return FFNQ_ERR_UNSUPPORTED;
+            const int rc = launch_shared_gu(sh, hidden, m, act, x, gps, gcs, sb, stream);
+            if (rc != FFNQ_OK) return rc;
         }
         if (!(tiled ? launch_gu_tiled(FMT_INT4, gc, stream, gp) : launch_gu(FMT_INT4, gc, u_est, moe_inter, stream, gp)))
             return FFNQ_ERR_UNSUPPORTED;
     }
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    // the shared expert's down: fp32 K-range partials, the seed is made by the reduction
+    // phase 2, fused: the shared expert's down, the routed down, the seeded
+    // reduction and the residual add in one launch
+    const MoeDownCfg md = moe_down_cfg(experts, n_experts, hidden, moe_inter, m, top_k, sh ? sh->ffn : nullptr,
+                                       sh ? sh->inter : 0);
+    if (md.ok) {
+        MoeDownParams q{};
+        q.tdown = static_cast<const uint8_t*>(experts->down.q);
+        q.tebytes = tiled_expert_bytes(experts->down);
+        q.N = hidden;
+        q.K = moe_inter;
+        q.act = gp.act_out;
+        q.act_rows = P;
+        q.plan = plan;
+        q.topk_ids = topk_ids;
+        q.topk_w = topk_w;
+        q.m = m;
+        q.top_k = top_k;
+        q.n_experts = n_experts;
+        if (sh) {
+            q.sh_tdown = static_cast<const uint8_t*>(sh->ffn->down.q);
+            q.sh_K = sh->inter;
+            q.sh_act = gps.act_out;
+            q.sh_logit = gps.logit;
+        } else {
+            q.seed = seed;
+        }
+        q.resid = resid;
+        if (!launch_moe_down(md, hidden, stream, q)) return FFNQ_ERR_UNSUPPORTED;
+        return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
+    }
+
+    // the shared expert's down: as ffnq_shared_expert runs it -- the burst
+    // kernel with its sigmoid-gate tail writing the bf16 seed, or fp32 K-range
+    // partials from which the routed reduction makes the seed
     KConfig dcs{};
     DownParams dps{};
+    const uint16_t* seed_rows = seed;
+    bool sh_part = false;
     if (sh) {
         dcs = dense_down_config(sh->ffn, hidden, sh->inter, m, cus, FFNQ_TAIL_SIGMOID_GATE);
-        dps = dense_down_params(sh->ffn, hidden, sh->inter, m, dcs, gps.act_out, nullptr,
-                                reinterpret_cast<float*>(sh->base + Ls.part),
-                                reinterpret_cast<const float*>(sh->base + Ls.logit), TAIL_PART);
+        const BurstCfg sdb = dense_down_burst(sh->ffn->down.fmt, hidden, sh->inter, m);
+        if (sdb.ok) {
+            uint16_t* sbuf = reinterpret_cast<uint16_t*>(base + L.seed);
+            dps = dense_down_params(sh->ffn, hidden, sh->inter, m, dcs, gps.act_out, sbuf,
+                                    reinterpret_cast<float*>(sh->base + Ls.part),
+                                    reinterpret_cast<const float*>(sh->base + Ls.logit), TAIL_SIGMOID);
+            dps.KG = 1;
+            if (!launch_down_burst(sh->ffn->down.fmt, sdb, hidden, stream, dps)) return FFNQ_ERR_UNSUPPORTED;
+            if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+            seed_rows = sbuf;
+        } else {
+            dps = dense_down_params(sh->ffn, hidden, sh->inter, m, dcs, gps.act_out, nullptr,
+                                    reinterpret_cast<float*>(sh->base + Ls.part),
+                                    reinterpret_cast<const float*>(sh->base + Ls.logit), TAIL_PART);
+            sh_part = true;
+        }
     }
 
     // phase 2: down per union entry and tile, d_p to pair_out
@@ -876,7 +1025,7 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     // partials, unchanged; one K range per workgroup) and both run in one launch.
     bool merged = false;
     KConfig dcs1 = dcs;
-    if (sh && tiled && is_tiled(sh->ffn->down.fmt) && is_int4(sh->ffn->down.fmt) && !dc.ts && dc.ks == 1 &&
+    if (sh_part && tiled && is_tiled(sh->ffn->down.fmt) && is_int4(sh->ffn->down.fmt) && !dc.ts && dc.ks == 1 &&
         dcs.nt == dc.nt && dcs.mt == dc.mt) {
         const TileGeo gs = tile_geo(FMT_INT4, hidden, sh->inter);
         dcs1.ts = 0;
@@ -886,7 +1035,7 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
                                     2 * dcs1.nt * red_lanes(dcs1.nt, dcs1.rows_cap)).total;
         merged = dcs1.lds <= kLdsBudget;
     }
-    if (sh && !merged) {
+    if (sh_part && !merged) {
         const int sdfmt = to_fmt(sh->ffn->down.fmt);
         if (!(is_tiled(sh->ffn->down.fmt) ? launch_down_tiled(sdfmt, dcs, stream, dps)
                                           : launch_down(sdfmt, dcs, 1, hidden, stream, dps)))
@@ -924,8 +1073,8 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     const long long total = (long long)m * hidden;
     const int rgrid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
     hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, dc.kg, topk_w, topk_ids,
-                       n_experts, sh ? nullptr : seed, resid, m, top_k, hidden, sh ? dps.part : nullptr,
-                       sh ? dcs.kg : 0, sh ? dps.logit : nullptr);
+                       n_experts, sh_part ? nullptr : seed_rows, resid, m, top_k, hidden, sh_part ? dps.part : nullptr,
+                       sh_part ? dcs.kg : 0, sh_part ? dps.logit : nullptr);
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
     return FFNQ_OK;
 }

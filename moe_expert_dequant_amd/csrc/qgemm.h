@@ -487,7 +487,6 @@ struct GUParams {
     const uint8_t* tup;
     long long tebytes;         // tiled bytes per expert
     int ks, grid;              // tiled kernels: waves per workgroup and gridDim.x, as launched
-    int upw;                   // burst kernels: K units per wave
 };
 
 template <int FMT, int NT, int MT>
@@ -633,7 +632,6 @@ struct DownParams {
     const uint8_t* tdown;      // tiled formats: packed down (expert 0)
     long long tebytes;         // tiled bytes per expert
     int ks, grid;              // tiled kernels: waves per workgroup and gridDim.x, as launched
-    int upw;                   // burst kernels: K units per wave
 };
 
 // by: the K range whose partial sum h is.

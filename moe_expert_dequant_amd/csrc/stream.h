@@ -1,16 +1,16 @@
-// stream.h -- burst kernels: the small-M dense projections with every weight
-// load of a wave issued at once.
+// stream.h -- burst kernels: the small-M projections with every weight load of
+// a wave issued at once, and the fused down + seeded reduction of a MoE layer.
 //
 // At one to four tokens the gate/up and down GEMVs of a layer ([llama/dense.rs]
-// encode_llama_layer_dense; [gemma4/shared_expert.rs] the shared-expert GEMVs)
-// are bound by how many bytes the chip keeps in flight, not by arithmetic.
-// Here a wave owns one 16-row tile over `upw` K units (INT4: a scale/zero step
-// and up to 8 code blocks of 128 inputs; INT8: up to 8 code blocks of 64) and
-// issues all of those 1 KB steps (per matrix) before it computes anything; the
-// activation slice of its units goes to wave-private LDS by direct
-// global->LDS loads issued just before them.  There is no ring to refill, no
-// workgroup barrier until the tile's waves meet in one LDS reduction, and the
-// code stays small enough to keep four waves per SIMD.
+// encode_llama_layer_dense; [gemma4/shared_expert.rs] the shared-expert GEMVs;
+// [qwen/moe_batch.rs] the routed phases) are bound by how many bytes the chip
+// keeps in flight, not by arithmetic.  Here a wave streams one or two "units"
+// -- one 16-row tile over one K unit (INT4: a scale/zero step and up to 8 code
+// blocks of 128 inputs; INT8: up to 8 code blocks of 64) -- and issues all of
+// their 1 KB steps (per matrix) before it computes anything; the activation
+// rows of its units and the scale/zero steps go to wave-private LDS by direct
+// global->LDS loads issued just before them.  There is no ring to refill and
+// no workgroup barrier until the tile's partial sums meet in LDS.
 //
 // Same arithmetic as the streaming kernels (tiled.h): codes widened to bf16
 // 128 + q, contracted on v_mfma_f32_16x16x32_bf16 against the activation rows,
@@ -23,18 +23,6 @@
 
 namespace ffnq {
 
-// One wave's K units and their activation rows.  R: activation rows used
-// (gate/up: the m token rows; down: the 2m hi/lo rows), at most 4, so the
-// results sit in lanes 0-15, register i = row i.  Lanes of MFMA row r >= R read
-// row r % R: rows of D depend only on the same rows of A, and rows >= R are
-// never read.
-struct BurstArgs {
-    const uint8_t* tq[2];     // tiled matrices
-    int N, K;                 // output rows, inputs
-    const uint16_t* src;      // activation rows [R][K] (x rows, or hi/lo act rows), row stride K
-    int upw, ks;              // K units per wave, waves per workgroup
-};
-
 template <int FMT>
 struct BurstGeo {
     static constexpr int BK = FmtT<FMT>::BK;                 // inputs per code block
@@ -46,86 +34,113 @@ struct BurstGeo {
     static constexpr int ROWB = UIN * 2 + 64;                // LDS bytes per staged row and unit (padded)
 };
 
-// LDS bytes of one wave (activation rows of its units, then their scale/zero
-// steps) and of the workgroup (waves, then the reduction area).
+// K units of a tiled matrix with k inputs.
+__host__ __device__ inline int burst_units(int fmt, int n, int k)
+{
+    const TileGeo g = tile_geo(fmt, n, k);
+    return fmt == FMT_INT4 ? g.ng : (g.nbk + 7) / 8;
+}
+
+// LDS bytes of one wave: the activation rows of its units, then their
+// scale/zero steps.
 __host__ __device__ inline int burst_wave_lds(int fmt, int nmat, int R, int upw)
 {
     const int uin = fmt == FMT_INT4 ? 1024 : 512;
     return upw * (R * (uin * 2 + 64) + (fmt == FMT_INT4 ? nmat * 1024 : 0));
 }
+// A workgroup of ks waves, each one unit, meeting in a [ks][nmat][4][16] reduction.
 __host__ __device__ inline int burst_lds(int fmt, int nmat, int R, int upw, int ks)
 {
     return ks * burst_wave_lds(fmt, nmat, R, upw) + ks * nmat * 4 * 16 * 4;
 }
 
-// The wave's contribution: acc[mt][i] for rows i < R in lanes 0-15 (lane = tile
-// row).  INT8 returns the unscaled sum of q*x (the code bias removed block by
-// block; the row scale is applied after the waves' sums meet).
+// One unit: tile `tile` of the matrices at tq (expert offset applied), K unit
+// u, against activation rows row[0..R) (each k bf16 long).  Lanes of MFMA row
+// r >= R read row r % R: rows of D depend only on the same rows of A, and rows
+// >= R are never read.
+struct BUnit {
+    const uint8_t* tq[2];
+    int n, k;                 // matrix rows and inputs
+    int tile, u;
+    const uint16_t* row[4];
+};
+
+// UPW units of one wave; acc[uu][mt][i] = the unit's sum for rows i < R in
+// lanes 0-15 (lane = tile row).  INT4 applies the group scales; INT8 returns
+// the unscaled sum of q*x (the code bias removed block by block; the row
+// scale is applied by the caller).  The first nvalid (uniform) units are
+// real; the code loads of the others repeat unit 0's, so that the number of
+// loads after the direct-to-LDS ones is a constant.
 template <int FMT, int NMAT, int R, int UPW>
-__device__ __forceinline__ void burst_wave(const BurstArgs& a, int tile, int w, uint8_t* wl, float (&acc)[NMAT][4])
+__device__ __forceinline__ void burst_wave(const BUnit (&un)[UPW], int nvalid, uint8_t* wl,
+                                           float (&acc)[UPW][NMAT][4])
 {
     using G = BurstGeo<FMT>;
-    constexpr int NL = UPW * G::UB * NMAT;       // code-step loads of the wave
-    constexpr int NX = UPW * R * G::CHUNKS;      // activation chunk loads
+    constexpr int NL = UPW * G::UB * NMAT;   // code-step loads of the wave
     const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
-    const TileGeo geo = tile_geo(FMT, a.N, a.K);
-    const int nun = FMT == FMT_INT4 ? geo.ng : (geo.nbk + G::UB - 1) / G::UB;
-    const int u0 = w * UPW;
+    uint8_t* szl = wl + UPW * R * G::ROWB;
 
-    // activation slice: rows r < R, inputs of units u0 .. u0+UPW-1, 1 KB per
-    // wave instruction; source addresses are clamped into the row (a chunk
-    // past K lands in LDS slots that are never read)
+    // activation rows of each unit, 1 KB per wave instruction; source
+    // addresses are clamped into the row (a chunk past k lands in LDS slots
+    // that are never read)
 #pragma unroll
-    for (int uu = 0; uu < UPW; ++uu)
+    for (int uu = 0; uu < UPW; ++uu) {
+        if (uu >= nvalid) break;   // uniform
+        const BUnit& U = un[uu];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < G::CHUNKS; ++c) {
-                const int k = min((u0 + uu) * G::UIN + c * 512 + lane * 8, a.K - 8);
-                lds_dma16(a.src + (size_t)r * a.K + k, lds_addr(wl + (uu * R + r) * G::ROWB + c * 1024));
+                const int kk = min(U.u * G::UIN + c * 512 + lane * 8, U.k - 8);
+                lds_dma16(U.row[r] + kk, lds_addr(wl + (uu * R + r) * G::ROWB + c * 1024));
             }
-    uint8_t* szl = wl + UPW * R * G::ROWB;
-    // INT4 scale/zero steps: straight to the wave's LDS as well (1 KB per
-    // matrix and unit, no registers held)
+    }
+    // INT4 scale/zero steps: straight to the wave's LDS as well
     if constexpr (FMT == FMT_INT4) {
 #pragma unroll
         for (int uu = 0; uu < UPW; ++uu) {
-            const int st = min((u0 + uu) * G::USTEPS, geo.steps - 1);
+            if (uu >= nvalid) break;
+            const BUnit& U = un[uu];
+            const TileGeo geo = tile_geo(FMT, U.n, U.k);
+            const int st = min(U.u * G::USTEPS, geo.steps - 1);
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt)
-                lds_dma16(a.tq[mt] + (size_t)tile * geo.tile_bytes + (size_t)st * kStep + lane * 16,
+                lds_dma16(U.tq[mt] + (size_t)U.tile * geo.tile_bytes + (size_t)st * kStep + lane * 16,
                           lds_addr(szl + (uu * NMAT + mt) * 1024));
         }
     }
-    // code steps: every one of the wave's units, clamped to the tile's last step
+    // code steps of every unit, clamped to the tile's last step
     u32x4 q[UPW][G::UB][NMAT];
 #pragma unroll
-    for (int uu = 0; uu < UPW; ++uu)
+    for (int uu = 0; uu < UPW; ++uu) {
+        const BUnit& U = un[uu < nvalid ? uu : 0];
+        const TileGeo geo = tile_geo(FMT, U.n, U.k);
 #pragma unroll
         for (int s = 0; s < G::UB; ++s) {
-            const int st = min((u0 + uu) * G::USTEPS + G::SZ + s, geo.steps - 1);
+            const int st = min(U.u * G::USTEPS + G::SZ + s, geo.steps - 1);
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt)
                 q[uu][s][mt] = __builtin_nontemporal_load(
-                    (const u32x4*)(a.tq[mt] + (size_t)tile * geo.tile_bytes + (size_t)st * kStep + lane * 16));
+                    (const u32x4*)(U.tq[mt] + (size_t)U.tile * geo.tile_bytes + (size_t)st * kStep + lane * 16));
         }
+    }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<NL>();   // the activation chunks and scale/zero steps (issued first) have landed
     __builtin_amdgcn_sched_barrier(0);
-    (void)NX;
 
     const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = 0.f;
     const int xrow = (lr % R) * G::ROWB;
 #pragma unroll
     for (int uu = 0; uu < UPW; ++uu) {
-        const int u = u0 + uu;
-        if (u >= nun) break;   // uniform
-        const int nb = FMT == FMT_INT4 ? min(G::UB, geo.nbk - 8 * u) : min(G::UB, geo.nbk - G::UB * u);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[uu][mt][i] = 0.f;
+        if (uu >= nvalid) continue;   // uniform
+        const BUnit& U = un[uu];
+        const int nbk = FMT == FMT_INT4 ? U.k / 128 : U.k / 64;
+        const int nb = min(G::UB, nbk - G::UB * U.u);
 #pragma unroll
         for (int bi = 0; bi < G::UB; ++bi) {
             if (bi >= nb) break;   // uniform
@@ -149,7 +164,7 @@ __device__ __forceinline__ void burst_wave(const BurstArgs& a, int tile, int w, 
                         const float sg = jg ? bf16hi_f32(sz[0]) : bf16lo_f32(sz[0]);
                         const float zg = (jg ? bf16hi_f32(sz[1]) : bf16lo_f32(sz[1])) + 128.0f;
 #pragma unroll
-                        for (int i = 0; i < R; ++i) acc[mt][i] = fmaf(sg, fmaf(-zg, o[jg][i], m[i]), acc[mt][i]);
+                        for (int i = 0; i < R; ++i) acc[uu][mt][i] = fmaf(sg, fmaf(-zg, o[jg][i], m[i]), acc[uu][mt][i]);
                     }
                 }
             } else {
@@ -166,124 +181,303 @@ __device__ __forceinline__ void burst_wave(const BurstArgs& a, int tile, int w, 
                         m = mfma_bf16(xs[d], u32x4{p0[0], p0[1], p1[0], p1[1]}, m);
                     }
 #pragma unroll
-                    for (int i = 0; i < R; ++i) acc[mt][i] += fmaf(-128.0f, o[i], m[i]);
+                    for (int i = 0; i < R; ++i) acc[uu][mt][i] += fmaf(-128.0f, o[i], m[i]);
                 }
             }
         }
     }
 }
 
-// The workgroup of one tile: its ks waves take units w*upw ..; their sums meet
-// in LDS in wave order; finish(i, n, v[NMAT]) gets row i, tile row n (< N).
-template <int FMT, int NMAT, int R, int UPW, typename Finish>
-__device__ __forceinline__ void burst_tile(const BurstArgs& a, int tile, Finish finish)
+// The fp32 row scale of tile row n of an INT8 tiled matrix (1 for INT4).
+template <int FMT>
+__device__ __forceinline__ float burst_row_scale(const uint8_t* tq, int n, int nrow, int k)
+{
+    if constexpr (FMT == FMT_INT8) {
+        const TileGeo geo = tile_geo(FMT, nrow, k);
+        return ((const float*)(tq + geo.scale_off))[n];
+    }
+    return 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// gate + up + activation.  A job is a dense FFN (the m token rows, one
+// workgroup per tile) or a routed phase 1 (one workgroup per (union entry,
+// tile), its rows the entry's pairs); a launch runs one job or two (a layer's
+// shared expert and its routed experts read the same x).  The waves of a
+// workgroup take the tile's K units, one each, and their sums meet in LDS in
+// wave order; f(gate) * up is written as the fp32 value's bf16 hi/lo pair
+// (act rows 2r, 2r+1 of row r: token or pair), in the natural order of a
+// tiled down matrix.  A job with gate_vec also forms the shared-expert gate
+// logits <gate_vec, x_t> in its workgroup 0.
+template <int FMT, int R>
+__device__ __forceinline__ void gu_burst_job(const GUParams& p, int bx)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wlds = burst_wave_lds(FMT, NMAT, R, UPW);
-    float acc[NMAT][4];
-    burst_wave<FMT, NMAT, R, UPW>(a, tile, w, smem + w * wlds, acc);
-    float* red = (float*)(smem + a.ks * wlds);   // [ks][NMAT][4][16]
+    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
+    const TileGeo geo = tile_geo(FMT, p.N, p.K);
+    const bool routed = p.plan != nullptr;
+    const int item = routed ? bx / geo.T : 0, tile = routed ? bx - item * geo.T : bx;
+    const PlanView pv{p.plan, p.m, p.top_k};
+    Item it{0, p.m, 0, true};
+    if (routed) {
+        if (item >= pv.n_union()) return;   // uniform: past this plan's union
+        it = resolve_item(pv, true, item, p.m, p.act_rows, p.topk_ids, p.n_experts);
+        if (!it.ok) return;
+    }
+    const int rows = min(it.R, R);   // the host sizes R for every item's rows
+    BUnit un[1];
+    un[0].tq[0] = p.tgate + (size_t)it.e * p.tebytes;
+    un[0].tq[1] = p.tup + (size_t)it.e * p.tebytes;
+    un[0].n = p.N;
+    un[0].k = p.K;
+    un[0].tile = tile;
+    un[0].u = w;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int rr = r < rows ? r : 0;
+        int tok = rr;
+        if (routed) {
+            const int pr = item_pair(pv, it, rr, p.act_rows);
+            tok = pr < 0 ? 0 : pr / p.top_k;
+        }
+        un[0].row[r] = p.x + (size_t)tok * p.K;
+    }
+    const int wlds = burst_wave_lds(FMT, 2, R, 1);
+    float acc[1][2][4];
+    burst_wave<FMT, 2, R, 1>(un, 1, smem + w * wlds, acc);
+    float* red = (float*)(smem + p.ks * wlds);   // [ks][2][4][16]
     if (lane < 16) {
 #pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < R; ++i) red[((w * NMAT + mt) * 4 + i) * 16 + lane] = acc[mt][i];
+            for (int i = 0; i < R; ++i) red[((w * 2 + mt) * 4 + i) * 16 + lane] = acc[0][mt][i];
     }
     __syncthreads();
-    const int tid = threadIdx.x;
-    if (tid < R * 16) {
+    if (tid < rows * 16) {
         const int i = tid >> 4, nl = tid & 15, n = tile * 16 + nl;
-        float v[NMAT];
+        float v[2];
 #pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) {
+        for (int mt = 0; mt < 2; ++mt) {
             float h = 0.f;
-            for (int ww = 0; ww < a.ks; ++ww) h += red[((ww * NMAT + mt) * 4 + i) * 16 + nl];
-            v[mt] = h;
+            for (int ww = 0; ww < p.ks; ++ww) h += red[((ww * 2 + mt) * 4 + i) * 16 + nl];
+            v[mt] = h * burst_row_scale<FMT>(un[0].tq[mt], n, p.N, p.K);
         }
-        if (FMT == FMT_INT8) {
-            const TileGeo geo = tile_geo(FMT, a.N, a.K);
-#pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) v[mt] *= ((const float*)(a.tq[mt] + geo.scale_off))[n];
+        int orow = i;
+        if (routed) orow = item_pair(pv, it, i, p.act_rows);
+        if (n < p.N && orow >= 0) {
+            const float y = act_f32(p.act, v[0]) * v[1];
+            uint16_t hi, lo;
+            split_bf16(y, hi, lo);
+            p.act_out[(size_t)(2 * orow) * p.N + n] = hi;
+            p.act_out[(size_t)(2 * orow + 1) * p.N + n] = lo;
         }
-        if (n < a.N) finish(i, n, v);
     }
-}
-
-// gate + up + activation for m = R tokens (one workgroup per tile): the
-// fp32 f(gate) * up as a bf16 hi/lo pair (act row 2t = hi, 2t+1 = lo), in the
-// natural order of a tiled down matrix.  With gate_vec, workgroup 0 also
-// forms the shared-expert gate logits <gate_vec, x_t>.
-template <int FMT, int R>
-__global__ void __launch_bounds__(1024) gu_burst_kernel(GUParams p)
-{
-    BurstArgs a{{p.tgate, p.tup}, p.N, p.K, p.x, p.upw, p.ks};
-    const int tile = blockIdx.x;
-    auto finish = [&](int i, int n, const float (&v)[2]) {
-        const float y = act_f32(p.act, v[0]) * v[1];
-        uint16_t hi, lo;
-        split_bf16(y, hi, lo);
-        p.act_out[(size_t)(2 * i) * p.N + n] = hi;
-        p.act_out[(size_t)(2 * i + 1) * p.N + n] = lo;
-    };
-    burst_tile<FMT, 2, R, 1>(a, tile, finish);   // one K unit per wave (the host launches upw == 1)
-    if (p.gate_vec != nullptr && tile == 0) {
-        const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-        for (int t = w; t < p.m; t += a.ks) {
-            double acc = 0.0;
+    if (p.gate_vec != nullptr && bx == 0) {
+        for (int t = w; t < p.m; t += p.ks) {
+            double s = 0.0;
             for (int i = lane; i < p.K; i += 64)
-                acc += (double)bf16_f32(p.gate_vec[i]) * (double)bf16_f32(p.x[(size_t)t * p.K + i]);
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (lane == 0) p.logit[t] = (float)acc;
+                s += (double)bf16_f32(p.gate_vec[i]) * (double)bf16_f32(p.x[(size_t)t * p.K + i]);
+            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+            if (lane == 0) p.logit[t] = (float)s;
         }
     }
 }
 
-// down + tail for m = R / 2 tokens (act rows 2t, 2t+1 = the hi/lo pair of
-// token t), one workgroup per tile over the whole K range, so the tail runs
-// here (down_finish with one K range).
+// One job (grid = its workgroups) or two (workgroups [0, na) job a, the rest
+// job b; both with the same format, rows and waves per workgroup).
+template <int FMT, int R>
+__global__ void __launch_bounds__(1024) gu_burst_kernel(GUParams a, GUParams b, int na)
+{
+    const int bx = (int)blockIdx.x;
+    if (bx < na)
+        gu_burst_job<FMT, R>(a, bx);
+    else
+        gu_burst_job<FMT, R>(b, bx - na);
+}
+
+// ---------------------------------------------------------------------------
+// Dense down + tail for m = R / 2 tokens (act rows 2t, 2t+1 = the hi/lo pair
+// of token t): one workgroup per tile over the whole K range, so the tail runs
+// here (down_finish with one K range).  The ks waves take the tile's K units
+// w, w + ks, ... in passes of one; each unit's sums go to its own LDS slot.
+// The hi and lo rows of a token are then summed separately in unit order,
+// added (hi + lo, as the streaming kernels do), scaled (INT8) and finished.
+__host__ __device__ inline int burst_down_lds(int fmt, int R, int ks, int units)
+{
+    return ks * burst_wave_lds(fmt, 1, R, 1) + units * 4 * 16 * 4;
+}
+
 template <int FMT, int R>
 __global__ void __launch_bounds__(1024) down_burst_kernel(DownParams p)
 {
     static_assert(R % 2 == 0, "hi/lo row pairs");
-    BurstArgs a{{p.tdown, nullptr}, p.N, p.K, p.act, p.upw, p.ks};
-    const int tile = blockIdx.x;
-    // the waves' sums meet in LDS; the hi and lo rows of token t are summed
-    // separately in wave order, then added (hi + lo, as the streaming kernels
-    // do), scaled (INT8) and finished by the tail
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    auto body = [&](auto upwc) {
-        constexpr int UPW = decltype(upwc)::value;
-        const int wlds = burst_wave_lds(FMT, 1, R, UPW);
-        float acc[1][4];
-        burst_wave<FMT, 1, R, UPW>(a, tile, w, smem + w * wlds, acc);
-        float* red = (float*)(smem + a.ks * wlds);   // [ks][4][16]
+    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int tile = blockIdx.x;
+    const int nu = burst_units(FMT, p.N, p.K);
+    const int wlds = burst_wave_lds(FMT, 1, R, 1);
+    float* red = (float*)(smem + p.ks * wlds);   // [nu][4][16]
+    for (int q = w; q < nu; q += p.ks) {
+        BUnit un[1];
+        un[0].tq[0] = p.tdown;
+        un[0].tq[1] = nullptr;
+        un[0].n = p.N;
+        un[0].k = p.K;
+        un[0].tile = tile;
+        un[0].u = q;
+#pragma unroll
+        for (int r = 0; r < R; ++r) un[0].row[r] = p.act + (size_t)r * p.K;
+        float acc[1][1][4];
+        burst_wave<FMT, 1, R, 1>(un, 1, smem + w * wlds, acc);
         if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) red[(w * 4 + i) * 16 + lane] = acc[0][i];
+            for (int i = 0; i < R; ++i) red[(q * 4 + i) * 16 + lane] = acc[0][0][i];
         }
-        __syncthreads();
-        const int tid = threadIdx.x;
-        if (tid < (R / 2) * 16) {
-            const int t = tid >> 4, nl = tid & 15, n = tile * 16 + nl;
-            float hh = 0.f, hl = 0.f;
-            for (int ww = 0; ww < a.ks; ++ww) {
-                hh += red[(ww * 4 + 2 * t) * 16 + nl];
-                hl += red[(ww * 4 + 2 * t + 1) * 16 + nl];
-            }
-            float h = hh + hl;
-            if (FMT == FMT_INT8) {
-                const TileGeo geo = tile_geo(FMT, a.N, a.K);
-                h *= ((const float*)(a.tq[0] + geo.scale_off))[n];
-            }
-            if (n < a.N) down_finish(p, 0, t, n, h);
+    }
+    __syncthreads();
+    if (tid < (R / 2) * 16) {
+        const int t = tid >> 4, nl = tid & 15, n = tile * 16 + nl;
+        float hh = 0.f, hl = 0.f;
+        for (int q = 0; q < nu; ++q) {
+            hh += red[(q * 4 + 2 * t) * 16 + nl];
+            hl += red[(q * 4 + 2 * t + 1) * 16 + nl];
         }
+        const float h = (hh + hl) * burst_row_scale<FMT>(p.tdown, n, p.N, p.K);
+        if (n < p.N) down_finish(p, 0, t, n, h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The routed down projection fused with the seeded phase-2 reduction and the
+// residual add ([qwen/moe_batch.rs] encode_qwen_layer_moe_batched: phase 2
+// starts its fp32 accumulator at the gated shared expert, then adds the ranks
+// in order; the tail is one raw residual add).  One workgroup per 16-row tile
+// of the output; its units are the shared expert's K units of that tile (rows:
+// the 2m hi/lo act rows) and, for each union entry of the plan, the expert's K
+// units of that tile (rows: the hi/lo rows of the entry's pairs), so each union
+// expert's tile is streamed once for all of its pairs.  A wave takes units w,
+// w + ks, ... in passes of one (its LDS holds one unit's rows); the units'
+// sums meet in LDS.  Then, per token and output row:
+// the seed (the shared expert's h * sigmoid(logit) rounded to bf16, as its own
+// tail writes it; or the caller's bf16 seed; or 0), acc += w_r * d_r for r =
+// 0..k-1 with product and sum each rounded to fp32, and resid = bf16(resid +
+// acc).  d_r and the shared h are (sum of the hi-row partials) + (sum of the
+// lo-row partials) in unit order -- the arithmetic of down_burst_kernel, so the
+// seed is bit for bit that of ffnq_shared_expert.  Pairs whose plan entry does
+// not name their expert, or whose id is out of range, add nothing.
+struct MoeDownParams {
+    const uint8_t* tdown;     // routed experts, tiled (expert 0)
+    long long tebytes;
+    int N, K;                 // hidden, moe_inter
+    const uint16_t* act;      // routed act rows [2 * act_rows][K]
+    int act_rows;             // m * top_k
+    const int32_t* plan;
+    const int32_t* topk_ids;
+    const float* topk_w;
+    int m, top_k, n_experts;
+    const uint8_t* sh_tdown;  // shared expert's tiled down [N][sh_K], or null
+    int sh_K;
+    const uint16_t* sh_act;   // its act rows [2m][sh_K]
+    const float* sh_logit;    // its gate logits [m]
+    const uint16_t* seed;     // bf16 [m][N] (no shared expert), or null for a zero seed
+    uint16_t* resid;          // bf16 [m][N], in/out
+    int ks;                   // waves per workgroup
+    int max_units;            // reduction slots: units of the largest union the plan can hold
+};
+
+template <int FMT, int R>
+__global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
+{
+    static_assert(R % 2 == 0, "hi/lo row pairs");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int tile = blockIdx.x;
+    const PlanView pv{p.plan, p.m, p.top_k};
+    const int U = pv.n_union();
+    const int ns = p.sh_tdown ? burst_units(FMT, p.N, p.sh_K) : 0;
+    const int nr = burst_units(FMT, p.N, p.K);
+    const int Q = min(ns + U * nr, p.max_units);
+    const int wlds = burst_wave_lds(FMT, 1, R, 1);
+    float* red = (float*)(smem + p.ks * wlds);   // [max_units][4][16]
+
+    // the wave's units q = w, w + ks, ... one pass each (one unit's rows staged at a time)
+    for (int q = w; q < Q; q += p.ks) {
+        BUnit un[1];
+        BUnit& B = un[0];
+        B.tile = tile;
+        B.n = p.N;
+        B.tq[1] = nullptr;
+        if (q < ns) {   // the shared expert's unit q
+            B.tq[0] = p.sh_tdown;
+            B.k = p.sh_K;
+            B.u = q;
+#pragma unroll
+            for (int r = 0; r < R; ++r) B.row[r] = p.sh_act + (size_t)min(r, 2 * p.m - 1) * p.sh_K;
+        } else {        // union entry g, unit j (an invalid entry streams expert 0 and is never summed)
+            const int g = (q - ns) / nr;
+            const Item it = resolve_item(pv, true, g, p.m, p.act_rows, p.topk_ids, p.n_experts);
+            B.tq[0] = p.tdown + (size_t)(it.ok ? it.e : 0) * p.tebytes;
+            B.k = p.K;
+            B.u = (q - ns) - g * nr;
+            const int npr = it.ok ? min(it.R, R / 2) : 1;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int pr = it.ok ? item_pair(pv, it, min(r >> 1, npr - 1), p.act_rows) : -1;
+                B.row[r] = p.act + (size_t)(2 * (pr < 0 ? 0 : pr) + (r & 1)) * p.K;
+            }
+        }
+        float acc[1][1][4];
+        burst_wave<FMT, 1, R, 1>(un, 1, smem + w * wlds, acc);
+        if (lane < 16) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) red[(q * 4 + i) * 16 + lane] = acc[0][0][i];
+        }
+    }
+    __syncthreads();
+    if (tid >= p.m * 16) return;
+    const int t = tid >> 4, nl = tid & 15, n = tile * 16 + nl;
+    if (n >= p.N) return;
+    // (sum of the units' rows 2j) + (sum of their rows 2j + 1) over units [q0, q0 + nu)
+    auto pair_sum = [&](int q0, int nu, int j) {
+        float hh = 0.f, hl = 0.f;
+        for (int q = q0; q < q0 + nu; ++q) {
+            hh += red[(q * 4 + 2 * j) * 16 + nl];
+            hl += red[(q * 4 + 2 * j + 1) * 16 + nl];
+        }
+        return hh + hl;
     };
-    if (a.upw == 1)
-        body(IntC<1>{});
-    else
-        body(IntC<2>{});
+    float acc0 = 0.0f;
+    if (ns > 0) {
+        const float h = pair_sum(0, ns, t) * burst_row_scale<FMT>(p.sh_tdown, n, p.N, p.sh_K);
+        const double sg = 1.0 / (1.0 + exp(-(double)p.sh_logit[t]));
+        acc0 = bf16_f32(bf16_from_f64((double)h * sg));
+    } else if (p.seed) {
+        acc0 = bf16_f32(p.seed[(size_t)t * p.N + n]);
+    }
+    // token t's sub-batch b: its union entries start at sub_union_begin[b]
+    const int32_t* sub_tok = p.plan + 1;
+    const int32_t* sub_uni = p.plan + (p.m + 2);
+    const int32_t* pslot = p.plan + (2 * p.m + 3 + p.m * p.top_k);
+    const int S = pv.n_sub();
+    int b = 0;
+    while (b + 1 < S && sub_tok[b + 1] <= t) ++b;
+    const int ub = min(max(sub_uni[b], 0), p.m * p.top_k);
+    for (int r = 0; r < p.top_k; ++r) {
+        const int pr = t * p.top_k + r;
+        const int e = p.topk_ids[pr];
+        if (e < 0 || e >= p.n_experts || pslot[pr] < 0) continue;
+        const int g = ub + pslot[pr];
+        if (g >= U || ns + (g + 1) * nr > Q) continue;
+        const Item it = resolve_item(pv, true, g, p.m, p.act_rows, p.topk_ids, p.n_experts);
+        if (!it.ok || it.e != e) continue;
+        int j = 0;   // the pair's place among the entry's pairs (ascending)
+        while (j < it.R && item_pair(pv, it, j, p.act_rows) != pr) ++j;
+        if (j >= it.R || j >= R / 2) continue;
+        const float d = pair_sum(ns + g * nr, nr, j) * burst_row_scale<FMT>(p.tdown + (size_t)e * p.tebytes, n, p.N, p.K);
+        acc0 = __fadd_rn(acc0, __fmul_rn(p.topk_w[pr], d));
+    }
+    uint16_t* o = p.resid + (size_t)t * p.N + n;
+    *o = bf16_from_f64((double)bf16_f32(*o) + (double)acc0);
 }
 
 }  // namespace ffnq
