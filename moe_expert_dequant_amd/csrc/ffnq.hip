@@ -811,15 +811,25 @@ bool launch_down_tiled2(const KConfig& a, const DownParams& pa, const KConfig& b
 // them in passes of one.  For m <= 2 tokens (2m activation rows per unit).
 struct MoeDownCfg {
     bool ok;
-    int R, ks, max_units;
+    int R, ks, upp, max_units;
     size_t lds;
 };
+
+constexpr size_t kLdsMax = 160 * 1024;   // LDS of one gfx950 CU (one workgroup per CU)
+// Units a wave of moe_down_kernel stages per pass: one.  (Two per pass, with
+// both units' loads in flight together, gave NaN outputs on the Mixtral-shaped
+// layer -- 28 units per tile -- for a reason not yet found; that path is off.)
+#ifndef FFNQ_MOE_DOWN_UPP
+#define FFNQ_MOE_DOWN_UPP 1
+#endif
 
 MoeDownCfg moe_down_cfg(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
                         const ffnq_ffn* shared, int shared_inter)
 {
-    MoeDownCfg c{false, 2 * m, 1, 0, 0};
-    if (!FFNQ_BURST || m > 2 || !is_tiled(experts->down.fmt) || !is_int4(experts->down.fmt)) return c;
+    MoeDownCfg c{false, 2 * m, 1, 1, 0, 0};
+    if (!FFNQ_BURST || m > 2 || (long long)m * top_k > 64 || !is_tiled(experts->down.fmt) ||
+        !is_int4(experts->down.fmt))
+        return c;
     int ns = 0;
     if (shared) {
         if (!is_tiled(shared->down.fmt) || !is_int4(shared->down.fmt)) return c;
@@ -831,17 +841,31 @@ MoeDownCfg moe_down_cfg(const ffnq_ffn* experts, int n_experts, int hidden, int 
     const long long units = ns + umax * nr;
     if (units > 64) return c;
     c.max_units = (int)units;
-    c.ks = (int)std::min<long long>(units, 16);
-    c.lds = (size_t)c.ks * burst_wave_lds(FMT_INT4, 1, c.R, 1) + (size_t)c.max_units * 4 * 16 * 4;
-    c.ok = c.lds <= kLdsBig;
+    // fewest passes (then most waves) among one or two units per pass that fit LDS
+    int best_passes = 1 << 30;
+    for (int upp = 1; upp <= FFNQ_MOE_DOWN_UPP; ++upp) {
+        for (int ks = (int)std::min<long long>(16, (units + upp - 1) / upp); ks >= 1; --ks) {
+            const size_t lds = (size_t)moe_down_lds(FMT_INT4, c.R, upp, ks, c.max_units);
+            if (lds > kLdsMax) continue;
+            const int passes = (int)((units + (long long)upp * ks - 1) / ((long long)upp * ks));
+            if (passes < best_passes) {
+                best_passes = passes;
+                c.upp = upp;
+                c.ks = ks;
+                c.lds = lds;
+                c.ok = true;
+            }
+            break;   // the most waves that fit for this upp
+        }
+    }
     return c;
 }
 
-#define FFNQ_MDN_CASE(R_)                                                                                      \
-    if (c.R == R_) {                                                                                           \
-        hipExtLaunchKernelGGL((moe_down_kernel<FMT_INT4, R_>), dim3((N + 15) / 16), dim3(64 * c.ks), c.lds, stream, \
-                              phase_event(2), phase_event(3), 0, q);                                           \
-        return true;                                                                                           \
+#define FFNQ_MDN_CASE(R_, UPP_)                                                                                 \
+    if (c.R == R_ && c.upp == UPP_) {                                                                           \
+        hipExtLaunchKernelGGL((moe_down_kernel<FMT_INT4, R_, UPP_>), dim3((N + 15) / 16), dim3(64 * c.ks), c.lds,  \
+                              stream, phase_event(2), phase_event(3), 0, q);                                    \
+        return true;                                                                                            \
     }
 
 bool launch_moe_down(const MoeDownCfg& c, int N, hipStream_t stream, const MoeDownParams& prm)
@@ -849,7 +873,7 @@ bool launch_moe_down(const MoeDownCfg& c, int N, hipStream_t stream, const MoeDo
     MoeDownParams q = prm;
     q.ks = c.ks;
     q.max_units = c.max_units;
-    FFNQ_MDN_CASE(2) FFNQ_MDN_CASE(4)
+    FFNQ_MDN_CASE(2, 1) FFNQ_MDN_CASE(4, 1)
     return false;
 }
 
@@ -916,7 +940,8 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
         gp.dfmt = FMT_NATURAL;
     }
     // the routed gate/up burst: every union entry holds at most m pairs (one per token)
-    const BurstCfg rb = burst_gu_cfg(experts->gate.fmt, hidden, moe_inter, m);
+    BurstCfg rb = burst_gu_cfg(experts->gate.fmt, hidden, moe_inter, m);
+    rb.ok = rb.ok && P <= 64;   // the burst kernel reads a plan entry's pairs with one ballot
     KConfig gcs{};
     GUParams gps{};
     DenseWs Ls{};

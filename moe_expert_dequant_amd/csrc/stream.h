@@ -200,6 +200,61 @@ __device__ __forceinline__ float burst_row_scale(const uint8_t* tq, int n, int n
 }
 
 // ---------------------------------------------------------------------------
+// A union entry of a routing plan (ffnq_moe_route's layout), for batches of
+// at most 64 pairs: its expert and the mask of its pairs (bit p = pair p, in
+// ascending order), from one round of independent loads -- the entry's
+// expert, every pair's expert id and the sub-batch bounds -- and ballots,
+// instead of walking the plan's arrays one dependent load after another.
+// An entry past the plan's union, an expert id out of range or an entry with
+// no pairs comes back with e = -1.  The pairs are those of the entry's
+// sub-batch whose id is the entry's expert (the plan's slot lists for a plan
+// that ffnq_moe_route wrote for these ids).
+struct PlanEntry {
+    int e;
+    uint64_t pairs;
+};
+
+__device__ __forceinline__ PlanEntry plan_entry(const int32_t* __restrict__ plan, const int32_t* __restrict__ ids,
+                                                int m, int k, int n_experts, int g)
+{
+    const int lane = threadIdx.x & 63, P = m * k;
+    const int32_t* sub_tok = plan + 1;
+    const int32_t* sub_uni = plan + (m + 2);
+    const int32_t* uexp = plan + (2 * m + 3);
+    const int n_sub = plan[0];
+    const int e = uexp[min(max(g, 0), P - 1)];
+    const int id = lane < P ? ids[lane] : -1;
+    const int st = lane <= m ? sub_tok[lane] : 0x7FFFFFFF;
+    const int su = lane <= m ? sub_uni[lane] : 0x7FFFFFFF;
+    PlanEntry r{-1, 0ull};
+    const int S = min(max(n_sub, 0), m);
+    // sub-batch b: the last of [0, S) whose first union entry is <= g
+    const uint64_t le = __ballot(lane < S && su <= g);
+    const int b = __popcll(le) - 1;
+    if (g < 0 || g >= P || e < 0 || e >= n_experts || b < 0) return r;
+    const int t0 = __builtin_amdgcn_readlane(st, b), t1 = __builtin_amdgcn_readlane(st, b + 1);
+    const int u1 = __builtin_amdgcn_readlane(su, b + 1);
+    if (g >= u1 || t0 < 0 || t1 > m || t0 >= t1) return r;
+    r.pairs = __ballot(lane < P && id == e && lane >= t0 * k && lane < t1 * k);
+    if (r.pairs) r.e = e;
+    return r;
+}
+
+// The index of the j-th set bit of a nonzero mask (j < popcount), or of the
+// last one when j is past it.
+__device__ __forceinline__ int nth_bit(uint64_t msk, int j)
+{
+    int b = __builtin_ctzll(msk);
+    for (int i = 0; i < j; ++i) {
+        const uint64_t rest = msk & (msk - 1);
+        if (!rest) break;
+        msk = rest;
+        b = __builtin_ctzll(msk);
+    }
+    return b;
+}
+
+// ---------------------------------------------------------------------------
 // gate + up + activation.  A job is a dense FFN (the m token rows, one
 // workgroup per tile) or a routed phase 1 (one workgroup per (union entry,
 // tile), its rows the entry's pairs); a launch runs one job or two (a layer's
@@ -217,17 +272,18 @@ __device__ __forceinline__ void gu_burst_job(const GUParams& p, int bx)
     const TileGeo geo = tile_geo(FMT, p.N, p.K);
     const bool routed = p.plan != nullptr;
     const int item = routed ? bx / geo.T : 0, tile = routed ? bx - item * geo.T : bx;
-    const PlanView pv{p.plan, p.m, p.top_k};
-    Item it{0, p.m, 0, true};
-    if (routed) {
-        if (item >= pv.n_union()) return;   // uniform: past this plan's union
-        it = resolve_item(pv, true, item, p.m, p.act_rows, p.topk_ids, p.n_experts);
-        if (!it.ok) return;
+    int e = 0, rows = p.m;
+    uint64_t pairs = 0;
+    if (routed) {   // union entry `item`: its expert and its pairs (at most m, one per token)
+        const PlanEntry pe = plan_entry(p.plan, p.topk_ids, p.m, p.top_k, p.n_experts, item);
+        if (pe.e < 0) return;   // uniform: past this plan's union, or not a valid entry
+        e = pe.e;
+        pairs = pe.pairs;
+        rows = min(__popcll(pairs), R);   // the host sizes R for every entry's rows
     }
-    const int rows = min(it.R, R);   // the host sizes R for every item's rows
     BUnit un[1];
-    un[0].tq[0] = p.tgate + (size_t)it.e * p.tebytes;
-    un[0].tq[1] = p.tup + (size_t)it.e * p.tebytes;
+    un[0].tq[0] = p.tgate + (size_t)e * p.tebytes;
+    un[0].tq[1] = p.tup + (size_t)e * p.tebytes;
     un[0].n = p.N;
     un[0].k = p.K;
     un[0].tile = tile;
@@ -235,11 +291,7 @@ __device__ __forceinline__ void gu_burst_job(const GUParams& p, int bx)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int rr = r < rows ? r : 0;
-        int tok = rr;
-        if (routed) {
-            const int pr = item_pair(pv, it, rr, p.act_rows);
-            tok = pr < 0 ? 0 : pr / p.top_k;
-        }
+        const int tok = routed ? nth_bit(pairs, rr) / p.top_k : rr;
         un[0].row[r] = p.x + (size_t)tok * p.K;
     }
     const int wlds = burst_wave_lds(FMT, 2, R, 1);
@@ -262,9 +314,8 @@ __device__ __forceinline__ void gu_burst_job(const GUParams& p, int bx)
             for (int ww = 0; ww < p.ks; ++ww) h += red[((ww * 2 + mt) * 4 + i) * 16 + nl];
             v[mt] = h * burst_row_scale<FMT>(un[0].tq[mt], n, p.N, p.K);
         }
-        int orow = i;
-        if (routed) orow = item_pair(pv, it, i, p.act_rows);
-        if (n < p.N && orow >= 0) {
+        const int orow = routed ? nth_bit(pairs, i) : i;
+        if (n < p.N) {
             const float y = act_f32(p.act, v[0]) * v[1];
             uint16_t hi, lo;
             split_bf16(y, hi, lo);
@@ -385,52 +436,124 @@ struct MoeDownParams {
     int max_units;            // reduction slots: units of the largest union the plan can hold
 };
 
-template <int FMT, int R>
+// LDS of moe_down_kernel: ks waves' staging (UPP units each), the
+// reduction slots, and the pair table (entry, place, weight; 64 pairs).
+__host__ __device__ inline int moe_down_lds(int fmt, int R, int upp, int ks, int max_units)
+{
+    return ks * burst_wave_lds(fmt, 1, R, upp) + max_units * 4 * 16 * 4 + 64 * 12;
+}
+
+template <int FMT, int R, int UPP>
 __global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
 {
     static_assert(R % 2 == 0, "hi/lo row pairs");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
     const int tile = blockIdx.x;
-    const PlanView pv{p.plan, p.m, p.top_k};
-    const int U = pv.n_union();
+    const int P = p.m * p.top_k;   // <= 64 (host)
     const int ns = p.sh_tdown ? burst_units(FMT, p.N, p.sh_K) : 0;
     const int nr = burst_units(FMT, p.N, p.K);
-    const int Q = min(ns + U * nr, p.max_units);
-    const int wlds = burst_wave_lds(FMT, 1, R, 1);
-    float* red = (float*)(smem + p.ks * wlds);   // [max_units][4][16]
+    const int Q = p.max_units;     // ns + nr * (largest possible union)
+    const int wlds = burst_wave_lds(FMT, 1, R, UPP);
+    float* red = (float*)(smem + p.ks * wlds);         // [Q][4][16]
+    int* tg = (int*)(red + (size_t)Q * 4 * 16);        // per pair: union entry (-1: adds nothing)
+    int* tj = tg + 64;                                 // its place among the entry's pairs
+    float* tw = (float*)(tj + 64);                     // its route weight
 
-    // the wave's units q = w, w + ks, ... one pass each (one unit's rows staged at a time)
-    for (int q = w; q < Q; q += p.ks) {
-        BUnit un[1];
-        BUnit& B = un[0];
-        B.tile = tile;
-        B.n = p.N;
-        B.tq[1] = nullptr;
-        if (q < ns) {   // the shared expert's unit q
-            B.tq[0] = p.sh_tdown;
-            B.k = p.sh_K;
-            B.u = q;
+    // the wave's units q = w + (pass * UPP + uu) * ks, UPP at a time; routed
+    // units of entries past the plan's union are skipped (uniform)
+    for (int q0 = w; q0 < Q; q0 += UPP * p.ks) {
+        BUnit un[UPP];
+        int qs[UPP];
+        int nvalid = 0;
 #pragma unroll
-            for (int r = 0; r < R; ++r) B.row[r] = p.sh_act + (size_t)min(r, 2 * p.m - 1) * p.sh_K;
-        } else {        // union entry g, unit j (an invalid entry streams expert 0 and is never summed)
-            const int g = (q - ns) / nr;
-            const Item it = resolve_item(pv, true, g, p.m, p.act_rows, p.topk_ids, p.n_experts);
-            B.tq[0] = p.tdown + (size_t)(it.ok ? it.e : 0) * p.tebytes;
+        for (int uu = 0; uu < UPP; ++uu) {
+            const int q = q0 + uu * p.ks;
+            qs[uu] = -1;
+            BUnit& B = un[uu];
+            B.tile = tile;
+            B.n = p.N;
+            B.tq[1] = nullptr;
+            B.tq[0] = p.tdown;
             B.k = p.K;
-            B.u = (q - ns) - g * nr;
-            const int npr = it.ok ? min(it.R, R / 2) : 1;
+            B.u = 0;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int pr = it.ok ? item_pair(pv, it, min(r >> 1, npr - 1), p.act_rows) : -1;
-                B.row[r] = p.act + (size_t)(2 * (pr < 0 ? 0 : pr) + (r & 1)) * p.K;
+            for (int r = 0; r < R; ++r) B.row[r] = p.act;
+            if (q >= Q || nvalid < uu) continue;   // units stay in order: valid ones first
+            if (q < ns) {   // the shared expert's unit q
+                B.tq[0] = p.sh_tdown;
+                B.k = p.sh_K;
+                B.u = q;
+#pragma unroll
+                for (int r = 0; r < R; ++r) B.row[r] = p.sh_act + (size_t)min(r, 2 * p.m - 1) * p.sh_K;
+            } else {        // union entry g, unit j
+                const int g = (q - ns) / nr;
+                const PlanEntry pe = plan_entry(p.plan, p.topk_ids, p.m, p.top_k, p.n_experts, g);
+                if (pe.e < 0) continue;
+                B.tq[0] = p.tdown + (size_t)pe.e * p.tebytes;
+                B.u = (q - ns) - g * nr;
+                const int npr = min(__popcll(pe.pairs), R / 2);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    B.row[r] = p.act + (size_t)(2 * nth_bit(pe.pairs, min(r >> 1, npr - 1)) + (r & 1)) * p.K;
             }
+            qs[uu] = q;
+            nvalid = uu + 1;
         }
-        float acc[1][1][4];
-        burst_wave<FMT, 1, R, 1>(un, 1, smem + w * wlds, acc);
+        if (nvalid == 0) break;   // uniform: the rest of this wave's units are past the union
+        float acc[UPP][1][4];
+        burst_wave<FMT, 1, R, UPP>(un, nvalid, smem + w * wlds, acc);
         if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) red[(q * 4 + i) * 16 + lane] = acc[0][0][i];
+            for (int uu = 0; uu < UPP; ++uu)
+                if (uu < nvalid) {
+#pragma unroll
+                    for (int i = 0; i < R; ++i) red[(qs[uu] * 4 + i) * 16 + lane] = acc[uu][0][i];
+                }
+        }
+    }
+    // the pair table, by wave 0 (one lane per pair): entry g of pair p is the
+    // entry of its token's sub-batch whose expert is the pair's; its place is
+    // the count of earlier pairs of that sub-batch with the same expert
+    if (w == 0) {
+        const int32_t* sub_tok = p.plan + 1;
+        const int32_t* sub_uni = p.plan + (p.m + 2);
+        const int32_t* uexp = p.plan + (2 * p.m + 3);
+        const int S = min(max(p.plan[0], 0), p.m);
+        const int id = lane < P ? p.topk_ids[lane] : -1;
+        const float wt = lane < P ? p.topk_w[lane] : 0.0f;
+        const int st = lane <= p.m ? sub_tok[lane] : 0x7FFFFFFF;
+        const int su = lane <= p.m ? sub_uni[lane] : 0x7FFFFFFF;
+        const int ue = lane < P ? uexp[lane] : -1;
+        const int t = lane / max(p.top_k, 1);
+        // sub-batch of token t: the last b < S with sub_tok[b] <= t
+        int b = -1;
+        for (int i = 0; i < S; ++i) b = __builtin_amdgcn_readlane(st, i) <= t ? i : b;
+        int g = -1, j = 0;
+        if (b >= 0 && id >= 0 && id < p.n_experts) {
+            int u0 = 0, u1 = 0, t0 = 0;
+            for (int i = 0; i < S + 1; ++i) {   // lane reads of the sub-batch bounds
+                const int sui = __builtin_amdgcn_readlane(su, i), sti = __builtin_amdgcn_readlane(st, i);
+                if (i == b) {
+                    u0 = sui;
+                    t0 = sti;
+                }
+                if (i == b + 1) u1 = sui;
+            }
+            for (int gg = 0; gg < P; ++gg) {
+                const int eg = __builtin_amdgcn_readlane(ue, gg);
+                if (gg >= u0 && gg < u1 && eg == id) g = gg;
+            }
+            for (int qq = 0; qq < P; ++qq) {
+                const int iq = __builtin_amdgcn_readlane(id, qq);
+                if (qq >= t0 * p.top_k && qq < lane && iq == id) ++j;
+            }
+        }
+        if (g >= 0 && (ns + (g + 1) * nr > Q || j >= R / 2)) g = -1;
+        if (lane < 64) {
+            tg[lane] = g;
+            tj[lane] = j;
+            tw[lane] = wt;
         }
     }
     __syncthreads();
@@ -454,27 +577,13 @@ __global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
     } else if (p.seed) {
         acc0 = bf16_f32(p.seed[(size_t)t * p.N + n]);
     }
-    // token t's sub-batch b: its union entries start at sub_union_begin[b]
-    const int32_t* sub_tok = p.plan + 1;
-    const int32_t* sub_uni = p.plan + (p.m + 2);
-    const int32_t* pslot = p.plan + (2 * p.m + 3 + p.m * p.top_k);
-    const int S = pv.n_sub();
-    int b = 0;
-    while (b + 1 < S && sub_tok[b + 1] <= t) ++b;
-    const int ub = min(max(sub_uni[b], 0), p.m * p.top_k);
     for (int r = 0; r < p.top_k; ++r) {
         const int pr = t * p.top_k + r;
-        const int e = p.topk_ids[pr];
-        if (e < 0 || e >= p.n_experts || pslot[pr] < 0) continue;
-        const int g = ub + pslot[pr];
-        if (g >= U || ns + (g + 1) * nr > Q) continue;
-        const Item it = resolve_item(pv, true, g, p.m, p.act_rows, p.topk_ids, p.n_experts);
-        if (!it.ok || it.e != e) continue;
-        int j = 0;   // the pair's place among the entry's pairs (ascending)
-        while (j < it.R && item_pair(pv, it, j, p.act_rows) != pr) ++j;
-        if (j >= it.R || j >= R / 2) continue;
-        const float d = pair_sum(ns + g * nr, nr, j) * burst_row_scale<FMT>(p.tdown + (size_t)e * p.tebytes, n, p.N, p.K);
-        acc0 = __fadd_rn(acc0, __fmul_rn(p.topk_w[pr], d));
+        const int g = tg[pr];
+        if (g < 0) continue;
+        const float d = pair_sum(ns + g * nr, nr, tj[pr]) *
+                        burst_row_scale<FMT>(p.tdown + (size_t)p.topk_ids[pr] * p.tebytes, n, p.N, p.K);
+        acc0 = __fadd_rn(acc0, __fmul_rn(tw[pr], d));
     }
     uint16_t* o = p.resid + (size_t)t * p.N + n;
     *o = bf16_from_f64((double)bf16_f32(*o) + (double)acc0);
