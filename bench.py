@@ -191,8 +191,9 @@ def run_phases(m: int, steps: int, warmup: int, copies: int, tiled: bool = True)
 # Steady-state timing of every workload shape: weight copies rotated so that the
 # bytes a call touches, over all copies, exceed twice the 256 MB Infinity Cache
 # (the 256x704 INT8 layer is L2-resident whatever is done, and is reported as a
-# latency).  Routed layers time the whole layer: shared expert (config 3),
-# router top-k and plan, routed phases 1 and 2.
+# latency).  Routed layers time the whole layer from the router logits
+# (ffnq_moe_layer_logits): router top-k and plan, shared expert (config 3),
+# routed phases 1 and 2.
 CONFIG_COPIES = {0: 1, 2: 6, 3: 6}
 
 
@@ -259,11 +260,10 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
         shs = None if sh is None else [fq.ffn_struct(d) for d in ([sh] + [_clone_mats(sh) for _ in range(copies - 1)])]
         gv = _dev16(inp["gate_vec"]) if sh is not None else None
 
-        def call(i):   # router top-k + plan, then the gated shared expert and the routed half in one call
-            fq.moe_route(logits, m, E, k, cap, ids, w, plan)
-            fq.moe_layer(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"],
-                         None if shs is None else shs[i % copies], cfg["shared_inter"] or 0, gv, x, ids, w, plan,
-                         resid, ws=ws)
+        def call(i):   # router top-k + plan, the gated shared expert and the routed half: one call
+            fq.moe_layer_logits(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"],
+                                None if shs is None else shs[i % copies], cfg["shared_inter"] or 0, gv, x, logits,
+                                cap, ids, w, plan, resid, ws=ws)
         counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
         extra = dict(union=union, sub_batches=n_sub, tokens_per_expert_min=int(counts[counts > 0].min()),
                      tokens_per_expert_max=int(counts.max()))
@@ -333,24 +333,95 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The oracle as it stands, single-threaded, on single tokens of the same workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_dense_by_rows(inp, c, pool, nthr: int):
+    """One token through the oracle's own step functions (gemv, act, residual),
+    each projection partitioned by output rows over `nthr` threads (ctypes
+    releases the GIL); the result is that of oracle.dense, bit for bit."""
+    import gen
+    import oracle
+
+    hidden, inter = c["hidden"], c["inter"]
+
+    def rows(mat, r0, r1):   # rows [r0, r1) of a row-major INT4 matrix (views, no copy)
+        return dict(fmt=mat["fmt"], n=r1 - r0, k=mat["k"], q=mat["q"][r0:r1], s=mat["s"][r0:r1], z=mat["z"][r0:r1])
+
+    def gemv_par(mat, x):
+        n = mat["n"]
+        b = [(n * i // nthr) // 16 * 16 for i in range(nthr)] + [n]
+        parts = list(pool.map(lambda i: oracle.gemv(rows(mat, b[i], b[i + 1]), x), range(nthr)))
+        return np.concatenate(parts)
+
+    f = inp["ffn"]
+    x = gen.bf16_to_f32(inp["x"][0]).astype(np.float64)
+    g = gemv_par(f["gate"], x)
+    u = gemv_par(f["up"], x)
+    a = np.array([oracle.act(c["act"], float(gi), float(ui)) for gi, ui in zip(g, u)], dtype=np.float64)
+    h = gemv_par(f["down"], a)
+    return np.array([oracle.residual(int(r), float(v)) for r, v in zip(inp["resid"][0], h)], np.uint16)
+
+
+def cpu_baseline(budget_s: float = 8.0):
+    """The oracle as it stands on the Llama-shaped layer: single-threaded and pinned to one core (M = 1 and
+    M = 4), then its step functions partitioned by output rows over every core this process may use (M = 1)."""
+    from concurrent.futures import ThreadPoolExecutor
     import gen
     import oracle
 
     c = gen.CONFIGS[1]
-    inp = gen.config_inputs(1, 1)
+    inp1 = gen.config_inputs(1, 1)
+    inp4 = gen.config_inputs(1, 4)
     oracle.lib()
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.dense(inp["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp["x"], inp["resid"])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 64:
-            break
-    return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{n} single-token calls (M=1) of the llama3-8b-shaped INT4 FFN layer, {el:.1f} s, one thread")
+    cpus = sorted(os.sched_getaffinity(0))
+    pinned = cpus[0]
+    os.sched_setaffinity(0, {pinned})
+    try:
+        n1, t0 = 0, time.perf_counter()
+        while True:
+            ref1 = oracle.dense(inp1["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp1["x"], inp1["resid"])
+            n1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= budget_s or n1 >= 64:
+                break
+        n4, t0 = 0, time.perf_counter()
+        while True:
+            oracle.dense(inp4["ffn"], c["hidden"], c["inter"], c["act"], c["tail"], inp4["x"], inp4["resid"])
+            n4 += 1
+            el4 = time.perf_counter() - t0
+            if el4 >= budget_s / 2 or n4 >= 16:
+                break
+    finally:
+        os.sched_setaffinity(0, set(cpus))
+    nthr = len(cpus)
+    with ThreadPoolExecutor(nthr) as pool:
+        got = _oracle_dense_by_rows(inp1, c, pool, nthr)
+        assert np.array_equal(got, ref1[0]), "row-partitioned oracle differs from the single-threaded one"
+        nm, t0 = 0, time.perf_counter()
+        while True:
+            _oracle_dense_by_rows(inp1, c, pool, nthr)
+            nm += 1
+            elm = time.perf_counter() - t0
+            if elm >= budget_s / 2 or nm >= 64:
+                break
+    return dict(value=n1 / el1, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n1} single-token calls (M=1) of the llama3-8b-shaped INT4 FFN layer, {el1:.1f} s, "
+                       f"one thread pinned to CPU {pinned}",
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count(), usable_cpus=nthr, pinned_cpu=pinned,
+                m4=dict(value=4 * n4 / el4, unit="tokens/s", cores=1, sample=f"{n4} calls at M=4, {el4:.1f} s"),
+                row_partitioned=dict(value=nm / elm, unit="tokens/s", cores=nthr,
+                                     sample=f"{nm} single-token calls, gate/up and down GEMVs split by output rows "
+                                            f"over {nthr} threads, bit-identical to the single-threaded oracle, "
+                                            f"{elm:.1f} s"))
 
 
 def main():

@@ -327,6 +327,27 @@ FFNQ_API int ffnq_moe_layer(const ffnq_ffn* experts, int n_experts, int hidden, 
                             const int32_t* plan, uint16_t* resid, void* ws, size_t* ws_bytes,
                             hipStream_t stream);
 
+/* ---- ffnq_moe_layer_logits -------------------------------------------------
+ * ffnq_moe_route followed by ffnq_moe_layer in one call ([qwen/moe_batch.rs]
+ * `encode_qwen_layer_moe_batched`: the router top-k over the batch's logits,
+ * then the gated shared expert and the routed half), with the same results
+ * bit for bit: topk_ids, topk_w and plan are written as ffnq_moe_route writes
+ * them, and resid as ffnq_moe_layer leaves it.  For small batches (tiled INT4
+ * experts, m <= 4, at most 64 pairs and m * n_experts <= 128 keys) the routing
+ * runs inside the routed gate/up launch, every workgroup of which repeats it,
+ * so the layer has no separate router launch; otherwise the router runs first
+ * on the same stream.
+ * Arguments: those of ffnq_moe_layer, plus logits / expert_scale / slot_cap /
+ * plan_bytes as for ffnq_moe_route; topk_ids, topk_w and plan are outputs here.
+ * Errors and the workspace contract: those of the two calls it replaces.
+ */
+FFNQ_API int ffnq_moe_layer_logits(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m,
+                                   int top_k, int act, const ffnq_ffn* shared, int shared_inter,
+                                   const uint16_t* shared_gate, const uint16_t* x, const float* logits,
+                                   const float* expert_scale, int slot_cap, int32_t* topk_ids, float* topk_w,
+                                   int32_t* plan, size_t plan_bytes, uint16_t* resid, void* ws, size_t* ws_bytes,
+                                   hipStream_t stream);
+
 /* ---- ffnq_packed_bytes / ffnq_pack -----------------------------------------
  * Bytes of one n x k matrix (one expert) in a tiled format; fmt may name the
  * row-major format or its tiled form.  0 for an unknown format or shape.

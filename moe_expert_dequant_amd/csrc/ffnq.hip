@@ -903,9 +903,35 @@ int launch_shared_gu(const LayerShared* sh, int hidden, int m, int act, const ui
 //     (moe_down_kernel);
 //   otherwise the streaming kernels, fp32 per-pair partials and
 //     moe_reduce_kernel.
+// Routing done inside the routed gate/up launch (ffnq_moe_layer_logits): the
+// logits, the expert scale and the slot cap; the ids, weights and plan are
+// written to the call's topk_ids / topk_w / plan.
+struct RouteIn {
+    const float* logits;
+    const float* scale;
+    int cap;
+};
+
+// Whether the routed gate/up launch routes the batch itself: every one of its
+// workgroups repeats the routing (ranking m * E keys), so only for batches
+// with few keys, where that costs less than a launch of its own.
+#ifndef FFNQ_ROUTE_IN_GU_KEYS
+#define FFNQ_ROUTE_IN_GU_KEYS 128   // measured: Qwen-shaped M = 1 (128 keys) gains ~4 us; M = 2 (256) does not
+#endif
+
+bool route_in_gu(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k)
+{
+    const long long P = (long long)m * top_k;
+    if (!FFNQ_BURST || !is_tiled(experts->gate.fmt) || !is_int4(experts->gate.fmt)) return false;
+    if (P > kSmallPairs || (long long)m * n_experts > std::min(kSmallKeys, FFNQ_ROUTE_IN_GU_KEYS)) return false;
+    const BurstCfg rb = burst_gu_cfg(experts->gate.fmt, hidden, moe_inter, m);
+    return rb.ok && small_route_lds(m, n_experts, top_k) <= kLdsBudget;
+}
+
 int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
                const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
-               const uint16_t* seed, uint16_t* resid, unsigned char* base, hipStream_t stream, const LayerShared* sh)
+               const uint16_t* seed, uint16_t* resid, unsigned char* base, hipStream_t stream, const LayerShared* sh,
+               const RouteIn* rin = nullptr)
 {
     const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
     const int cus = device_cus();
@@ -942,6 +968,16 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     // the routed gate/up burst: every union entry holds at most m pairs (one per token)
     BurstCfg rb = burst_gu_cfg(experts->gate.fmt, hidden, moe_inter, m);
     rb.ok = rb.ok && P <= 64;   // the burst kernel reads a plan entry's pairs with one ballot
+    if (rin) {   // the caller checked route_in_gu: the routed job routes the batch first
+        gp.logits = rin->logits;
+        gp.escale = rin->scale;
+        gp.cap = rin->cap;
+        gp.ids_out = const_cast<int32_t*>(topk_ids);
+        gp.w_out = const_cast<float*>(topk_w);
+        gp.plan_out = const_cast<int32_t*>(plan);
+        rb.lds = std::max(rb.lds, small_route_lds(m, n_experts, top_k));
+        if (!rb.ok) return FFNQ_ERR_UNSUPPORTED;
+    }
     KConfig gcs{};
     GUParams gps{};
     DenseWs Ls{};
@@ -1105,6 +1141,100 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
 }
 
 // ---------------------------------------------------------------------------
+// router top-k and plan (ffnq_moe_route, and ffnq_moe_layer_logits when it
+// cannot route inside the gate/up launch)
+
+int check_route(const float* logits, const float* expert_scale, int m, int n_experts, int top_k, int slot_cap,
+                const int32_t* topk_ids, const float* topk_w, const int32_t* plan, size_t plan_bytes)
+{
+    if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
+    if (!logits || !topk_ids || !topk_w || !plan) return FFNQ_ERR_INVALID;
+    if (misaligned(logits) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(plan) ||
+        (expert_scale && misaligned(expert_scale)))
+        return FFNQ_ERR_INVALID;
+    if (n_experts > FFNQ_MAX_EXPERTS) return FFNQ_ERR_UNSUPPORTED;
+    if (slot_cap > FFNQ_MAX_SLOTS) return FFNQ_ERR_UNSUPPORTED;
+    if (slot_cap < top_k) return FFNQ_ERR_CAPACITY;
+    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
+    if (plan_bytes < (size_t)FFNQ_PLAN_INTS((size_t)m, (size_t)top_k) * 4) return FFNQ_ERR_WORKSPACE;
+    return FFNQ_OK;
+}
+
+// A checked route with m > 0: the small-batch kernel when the batch has at most
+// 256 keys (one workgroup, a thread per key; measured faster there, slower
+// than route_kernel's wave per token at 512 keys), else route_kernel.
+constexpr int kSmallRouteKeys = 256;
+int launch_route(const float* logits, const float* expert_scale, int m, int n_experts, int top_k, int slot_cap,
+                 int32_t* topk_ids, float* topk_w, int32_t* plan, hipStream_t stream)
+{
+    RouteParams p{logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan};
+    const long long P = (long long)m * top_k;
+    const size_t slds = small_route_lds(m, n_experts, top_k);
+    if (P <= kSmallPairs && (long long)m * n_experts <= kSmallRouteKeys && slds <= kLdsBudget) {
+        hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(256), slds, stream, p);
+    } else if (P <= kIdsCache && (long long)m * n_experts <= kLgCache) {
+        hipLaunchKernelGGL(route_kernel<true>, dim3(1), dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(route_kernel<false>, dim3(1), dim3(256), 0, stream, p);
+    }
+    return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
+}
+
+// ffnq_moe_layer, and ffnq_moe_layer_logits (rin: route the batch first; in
+// the routed gate/up launch when it can, else with its own launch).
+int moe_layer_common(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
+                     const ffnq_ffn* shared, int shared_inter, const uint16_t* shared_gate, const uint16_t* x,
+                     const int32_t* topk_ids, const float* topk_w, const int32_t* plan, size_t plan_bytes,
+                     uint16_t* resid, void* ws, size_t* ws_bytes, hipStream_t stream, const RouteIn* rin)
+{
+    if (!ws_bytes) return FFNQ_ERR_INVALID;
+    if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
+    int rc = check_ffn(experts, hidden, moe_inter);
+    if (rc != FFNQ_OK) return rc;
+    if (!is_int4(experts->gate.fmt) || !is_int4(experts->up.fmt) || !is_int4(experts->down.fmt))
+        return FFNQ_ERR_UNSUPPORTED;
+    if (shared) {
+        rc = check_ffn(shared, hidden, shared_inter);
+        if (rc != FFNQ_OK) return rc;
+        if (!shared_gate || misaligned(shared_gate)) return FFNQ_ERR_INVALID;
+    }
+    if (act != FFNQ_ACT_SILU && act != FFNQ_ACT_GELU_TANH) return FFNQ_ERR_UNSUPPORTED;
+    if (!x || !topk_ids || !topk_w || !plan || !resid) return FFNQ_ERR_INVALID;
+    if (misaligned(x) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(plan) || misaligned(resid))
+        return FFNQ_ERR_INVALID;
+    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
+    const size_t rows_bytes = (size_t)m * hidden * 2;
+    if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
+    if (rin) {
+        rc = check_route(rin->logits, rin->scale, m, n_experts, top_k, rin->cap, topk_ids, topk_w, plan, plan_bytes);
+        if (rc != FFNQ_OK) return rc;
+    }
+    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
+    const size_t shared_off = align_up(L.total, 256);
+    const size_t total = m == 0 ? 0
+                                : shared_off + (shared ? dense_ws(shared->down.fmt, hidden, shared_inter, m,
+                                                                  FFNQ_TAIL_SIGMOID_GATE, true).total
+                                                       : 0);
+    if (!ws) {
+        *ws_bytes = total;
+        return FFNQ_OK;
+    }
+    if (*ws_bytes < total) return FFNQ_ERR_WORKSPACE;
+    if (misaligned(ws)) return FFNQ_ERR_INVALID;
+    if (m == 0) return FFNQ_OK;
+    if (rin && !route_in_gu(experts, n_experts, hidden, moe_inter, m, top_k)) {
+        rc = launch_route(rin->logits, rin->scale, m, n_experts, top_k, rin->cap, const_cast<int32_t*>(topk_ids),
+                          const_cast<float*>(topk_w), const_cast<int32_t*>(plan), stream);
+        if (rc != FFNQ_OK) return rc;
+        rin = nullptr;
+    }
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    const LayerShared lsh{shared, shared_inter, shared_gate, base + shared_off};
+    return run_routed(experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan, nullptr, resid,
+                      base, stream, shared ? &lsh : nullptr, rin);
+}
+
+// ---------------------------------------------------------------------------
 // The allocation-free dense call (ffnq_dense_noalloc) keeps its workspace in
 // this file-scope device array: every GPU the library runs on holds one copy,
 // for the life of the process.  Host code never passes the array's name to a
@@ -1246,24 +1376,9 @@ int ffnq_router_logits(const uint16_t* x, const uint16_t* w, int m, int hidden, 
 int ffnq_moe_route(const float* logits, const float* expert_scale, int m, int n_experts, int top_k, int slot_cap,
                    int32_t* topk_ids, float* topk_w, int32_t* plan, size_t plan_bytes, hipStream_t stream)
 {
-    if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
-    if (!logits || !topk_ids || !topk_w || !plan) return FFNQ_ERR_INVALID;
-    if (misaligned(logits) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(plan) ||
-        (expert_scale && misaligned(expert_scale)))
-        return FFNQ_ERR_INVALID;
-    if (n_experts > FFNQ_MAX_EXPERTS) return FFNQ_ERR_UNSUPPORTED;
-    if (slot_cap > FFNQ_MAX_SLOTS) return FFNQ_ERR_UNSUPPORTED;
-    if (slot_cap < top_k) return FFNQ_ERR_CAPACITY;
-    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
-    if (plan_bytes < (size_t)FFNQ_PLAN_INTS((size_t)m, (size_t)top_k) * 4) return FFNQ_ERR_WORKSPACE;
-    if (m == 0) return FFNQ_OK;
-    RouteParams p{logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan};
-    const bool small = (long long)m * top_k <= kIdsCache && (long long)m * n_experts <= kLgCache;
-    if (small)
-        hipLaunchKernelGGL(route_kernel<true>, dim3(1), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(route_kernel<false>, dim3(1), dim3(256), 0, stream, p);
-    return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
+    const int rc = check_route(logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan, plan_bytes);
+    if (rc != FFNQ_OK || m == 0) return rc;
+    return launch_route(logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan, stream);
 }
 
 int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
@@ -1303,41 +1418,19 @@ int ffnq_moe_layer(const ffnq_ffn* experts, int n_experts, int hidden, int moe_i
                    const int32_t* topk_ids, const float* topk_w, const int32_t* plan, uint16_t* resid, void* ws,
                    size_t* ws_bytes, hipStream_t stream)
 {
-    if (!ws_bytes) return FFNQ_ERR_INVALID;
-    if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
-    int rc = check_ffn(experts, hidden, moe_inter);
-    if (rc != FFNQ_OK) return rc;
-    if (!is_int4(experts->gate.fmt) || !is_int4(experts->up.fmt) || !is_int4(experts->down.fmt))
-        return FFNQ_ERR_UNSUPPORTED;
-    if (shared) {
-        rc = check_ffn(shared, hidden, shared_inter);
-        if (rc != FFNQ_OK) return rc;
-        if (!shared_gate || misaligned(shared_gate)) return FFNQ_ERR_INVALID;
-    }
-    if (act != FFNQ_ACT_SILU && act != FFNQ_ACT_GELU_TANH) return FFNQ_ERR_UNSUPPORTED;
-    if (!x || !topk_ids || !topk_w || !plan || !resid) return FFNQ_ERR_INVALID;
-    if (misaligned(x) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(plan) || misaligned(resid))
-        return FFNQ_ERR_INVALID;
-    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
-    const size_t rows_bytes = (size_t)m * hidden * 2;
-    if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
-    const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
-    const size_t shared_off = align_up(L.total, 256);
-    const size_t total = m == 0 ? 0
-                                : shared_off + (shared ? dense_ws(shared->down.fmt, hidden, shared_inter, m,
-                                                                  FFNQ_TAIL_SIGMOID_GATE, true).total
-                                                       : 0);
-    if (!ws) {
-        *ws_bytes = total;
-        return FFNQ_OK;
-    }
-    if (*ws_bytes < total) return FFNQ_ERR_WORKSPACE;
-    if (misaligned(ws)) return FFNQ_ERR_INVALID;
-    if (m == 0) return FFNQ_OK;
-    unsigned char* base = static_cast<unsigned char*>(ws);
-    const LayerShared lsh{shared, shared_inter, shared_gate, base + shared_off};
-    return run_routed(experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan, nullptr, resid,
-                      base, stream, shared ? &lsh : nullptr);
+    return moe_layer_common(experts, n_experts, hidden, moe_inter, m, top_k, act, shared, shared_inter, shared_gate,
+                            x, topk_ids, topk_w, plan, 0, resid, ws, ws_bytes, stream, nullptr);
+}
+
+int ffnq_moe_layer_logits(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
+                          int act, const ffnq_ffn* shared, int shared_inter, const uint16_t* shared_gate,
+                          const uint16_t* x, const float* logits, const float* expert_scale, int slot_cap,
+                          int32_t* topk_ids, float* topk_w, int32_t* plan, size_t plan_bytes, uint16_t* resid,
+                          void* ws, size_t* ws_bytes, hipStream_t stream)
+{
+    const RouteIn rin{logits, expert_scale, slot_cap};
+    return moe_layer_common(experts, n_experts, hidden, moe_inter, m, top_k, act, shared, shared_inter, shared_gate,
+                            x, topk_ids, topk_w, plan, plan_bytes, resid, ws, ws_bytes, stream, &rin);
 }
 
 }  // extern "C"

@@ -487,6 +487,13 @@ struct GUParams {
     const uint8_t* tup;
     long long tebytes;         // tiled bytes per expert
     int ks, grid;              // tiled kernels: waves per workgroup and gridDim.x, as launched
+    // routed burst job that routes its own batch (the plan is then written by it):
+    const float* logits;       // [m][n_experts] router logits, or null (plan given)
+    const float* escale;       // [n_experts] per-expert scale, or null
+    int cap;                   // slot cap of the sub-batches
+    int32_t* ids_out;          // [m][top_k] route ids, written by the job's workgroup 0
+    float* w_out;              // [m][top_k] route weights, likewise
+    int32_t* plan_out;         // the plan, likewise (plan == plan_out)
 };
 
 template <int FMT, int NT, int MT>

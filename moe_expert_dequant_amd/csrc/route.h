@@ -117,6 +117,175 @@ struct IntC {
     static constexpr int value = N;
 };
 
+// ---------------------------------------------------------------------------
+// Routing of a small batch (m * E <= kSmallKeys keys, m * k <= 64 pairs) by
+// one workgroup of nt >= 64 threads, entirely in LDS: the top-k of every token
+// with its weights, and the plan.  The same selection, weights and plan as
+// route_kernel (and as the definition: rank by key, weights exp(l_r - l_0)
+// over their sum in rank order times the expert scale, greedy maximal
+// sub-batches with first-appearance slots).  A thread per (token, expert) key
+// counts the keys above it; a thread per pair forms its exponential, then its
+// weight; wave 0 builds the plan with one lane per pair, walking the tokens
+// in order for the greedy sub-batches.  Ends with a workgroup barrier; the
+// results are in the LDS arrays of SmallRoute.
+constexpr int kSmallKeys = 2048;
+constexpr int kSmallPairs = 64;
+
+struct SmallRoute {
+    uint64_t* keys;   // [m][E]
+    int* sel;         // [P] expert of pair p = t*k + r
+    float* sell;      // [P] its logit (from its key: NaN as -inf, -0 as +0)
+    double* ex;       // [P] exp(l_r - l_0)
+    float* w;         // [P] route weight
+    int* plan;        // [FFNQ_PLAN_INTS(m, k)]: the plan, -1 in unused entries
+};
+
+__host__ __device__ inline size_t small_route_lds(int m, int E, int k)
+{
+    const int P = m * k;
+    return (size_t)m * E * 8 + (size_t)P * 8 + (size_t)P * 4 * 3 + (size_t)(2 * m + 4 + 4 * P) * 4 + 64;
+}
+
+__device__ inline SmallRoute small_route_layout(unsigned char* base, int m, int E, int k)
+{
+    const int P = m * k;
+    SmallRoute L;
+    L.keys = (uint64_t*)base;
+    L.ex = (double*)(base + (size_t)m * E * 8);
+    L.sel = (int*)(L.ex + P);
+    L.sell = (float*)(L.sel + P);
+    L.w = L.sell + P;
+    L.plan = (int*)(L.w + P);
+    return L;
+}
+
+__device__ void route_small(const float* __restrict__ logits, const float* __restrict__ scale, int m, int E, int k,
+                            int cap, const SmallRoute& L)
+{
+    const int tid = threadIdx.x, nt = blockDim.x, P = m * k;
+    for (int i = tid; i < m * E; i += nt) {
+        const int t = i / E;
+        L.keys[i] = route_key(logits[i], i - t * E);
+    }
+    const int total = 2 * m + 4 + 4 * P;
+    for (int i = tid; i < total; i += nt) L.plan[i] = -1;
+    __syncthreads();
+    // rank of each key among its token's keys: the keys above it (keys are distinct)
+    for (int i = tid; i < m * E; i += nt) {
+        const int t = i / E;
+        const uint64_t key = L.keys[i];
+        const uint64_t* row = L.keys + (size_t)t * E;
+        int rank = 0;
+        for (int e2 = 0; e2 < E; ++e2) rank += row[e2] > key ? 1 : 0;
+        if (rank < k) {
+            L.sel[t * k + rank] = i - t * E;
+            L.sell[t * k + rank] = route_key_logit(key);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < P; i += nt) {
+        const int t = i / k;
+        const float l = L.sell[i], f0 = L.sell[t * k];
+        const double lr = (l != l) ? -INFINITY : (double)l;
+        const double l0 = (f0 != f0) ? -INFINITY : (double)f0;
+        L.ex[i] = (lr == l0) ? 1.0 : exp(lr - l0);
+    }
+    __syncthreads();
+    for (int i = tid; i < P; i += nt) {
+        const int t = i / k;
+        double sum = 0.0;
+        for (int r = 0; r < k; ++r) sum += L.ex[t * k + r];
+        const double sc = scale ? (double)scale[L.sel[i]] : 1.0;
+        L.w[i] = (float)(L.ex[i] / sum * sc);
+    }
+    // the plan: wave 0, lane = pair
+    if (tid < 64) {
+        const int lane = tid;
+        const bool valid = lane < P;
+        const int id = valid ? L.sel[lane] : -1;
+        const int tok = lane / k;
+        int32_t* sub_tok = L.plan + 1;
+        int32_t* sub_uni = L.plan + (m + 2);
+        int32_t* uexp = L.plan + (2 * m + 3);
+        int32_t* pslot = L.plan + (2 * m + 3 + P);
+        int32_t* spb = L.plan + (2 * m + 3 + 2 * P);
+        int32_t* sp = L.plan + (2 * m + 4 + 3 * P);
+        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        int S = 0, s = 0, usize = 0, base = 0;
+        int my_sb = -1, my_first = 0, my_slot = -1, my_base = 0;
+        for (int t = 0; t < m; ++t) {
+            const bool in_t = valid && tok == t;
+            bool seen = false;   // my expert already in the current sub-batch's earlier tokens
+            for (int q = s * k; q < t * k; ++q) seen |= __builtin_amdgcn_readlane(id, q) == id;
+            uint64_t fresh = __ballot(in_t && !seen);
+            int nf = __popcll(fresh);
+            if (usize + nf > cap) {   // close [s, t): the greedy sub-batch is maximal
+                if (lane == 0) {
+                    sub_tok[S] = s;
+                    sub_uni[S] = base;
+                }
+                ++S;
+                base += usize;
+                usize = 0;
+                s = t;
+                fresh = __ballot(in_t);
+                nf = __popcll(fresh);
+            }
+            if (in_t) {
+                my_sb = S;
+                my_base = base;
+                my_first = (int)((fresh >> lane) & 1ull);
+                if (my_first) my_slot = usize + __popcll(fresh & below);
+            }
+            usize += nf;
+        }
+        if (lane == 0) {
+            sub_tok[S] = s;
+            sub_uni[S] = base;
+            sub_tok[S + 1] = m;
+            sub_uni[S + 1] = base + usize;
+            L.plan[0] = S + 1;
+        }
+        // a repeated expert takes the slot of its first pair in the sub-batch
+        for (int q = 0; q < P; ++q) {
+            const int qid = __builtin_amdgcn_readlane(id, q), qsb = __builtin_amdgcn_readlane(my_sb, q);
+            const int qf = __builtin_amdgcn_readlane(my_first, q), qs = __builtin_amdgcn_readlane(my_slot, q);
+            if (valid && !my_first && qf && qsb == my_sb && qid == id) my_slot = qs;
+        }
+        const int my_g = valid ? my_base + my_slot : 0x7FFFFFFF;
+        int before = 0, same = 0;   // pairs of earlier entries; earlier pairs of my entry
+        for (int q = 0; q < P; ++q) {
+            const int qg = __builtin_amdgcn_readlane(my_g, q);
+            before += qg < my_g ? 1 : 0;
+            same += (q < lane && qg == my_g) ? 1 : 0;
+        }
+        if (valid) {
+            pslot[lane] = my_slot;
+            sp[before + same] = lane;
+            if (my_first) {
+                uexp[my_g] = id;
+                spb[my_g] = before;
+            }
+        }
+        if (lane == 0) spb[base + usize] = P;
+    }
+    __syncthreads();
+}
+
+// ffnq_moe_route for a small batch: route_small, then the outputs to global memory.
+__global__ void __launch_bounds__(256) route_small_kernel(RouteParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const SmallRoute L = small_route_layout(smem, p.m, p.E, p.k);
+    route_small(p.logits, p.scale, p.m, p.E, p.k, p.cap, L);
+    const int P = p.m * p.k, total = 2 * p.m + 4 + 4 * P;
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        p.ids[i] = L.sel[i];
+        p.w[i] = L.w[i];
+    }
+    for (int i = threadIdx.x; i < total; i += blockDim.x) p.plan[i] = L.plan[i];
+}
+
 // SMALL: the batch's logits (m * E <= kLgCache) and chosen ids (m * k <=
 // kIdsCache) are held in LDS; a compile-time choice, because a run-time select
 // between an LDS and a global source compiles to one flat load, and a flat load

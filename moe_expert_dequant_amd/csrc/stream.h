@@ -19,6 +19,7 @@
 // (and so the order of the fp32 partial sums) differs, and the INT8 code bias
 // is removed per block of 64 inputs rather than once per K range.
 #pragma once
+#include "route.h"
 #include "tiled.h"
 
 namespace ffnq {
@@ -274,7 +275,32 @@ __device__ __forceinline__ void gu_burst_job(const GUParams& p, int bx)
     const int item = routed ? bx / geo.T : 0, tile = routed ? bx - item * geo.T : bx;
     int e = 0, rows = p.m;
     uint64_t pairs = 0;
-    if (routed) {   // union entry `item`: its expert and its pairs (at most m, one per token)
+    if (routed && p.logits) {
+        // route the batch here (every workgroup of the job, in LDS): the entry's
+        // expert and pairs from the plan; workgroup 0 writes ids, weights and plan
+        const int P = p.m * p.top_k;
+        const SmallRoute L = small_route_layout(smem, p.m, p.n_experts, p.top_k);
+        route_small(p.logits, p.escale, p.m, p.n_experts, p.top_k, p.cap, L);
+        const int32_t* lplan = L.plan;
+        const int U = lplan[p.m + 2 + lplan[0]];   // sub_union_begin[n_sub]: the union's size
+        if (bx == 0) {
+            const int total = 2 * p.m + 4 + 4 * P;
+            for (int i = tid; i < P; i += blockDim.x) {
+                p.ids_out[i] = L.sel[i];
+                p.w_out[i] = L.w[i];
+            }
+            for (int i = tid; i < total; i += blockDim.x) p.plan_out[i] = lplan[i];
+        }
+        if (item < U) {
+            e = lplan[2 * p.m + 3 + item];
+            const int32_t* spb = lplan + (2 * p.m + 3 + 2 * P);
+            const int32_t* sp = lplan + (2 * p.m + 4 + 3 * P);
+            for (int i = spb[item]; i < spb[item + 1]; ++i) pairs |= 1ull << sp[i];
+        }
+        __syncthreads();   // the LDS is the burst's staging from here on
+        if (item >= U || e < 0 || e >= p.n_experts || pairs == 0ull) return;   // uniform
+        rows = min(__popcll(pairs), R);
+    } else if (routed) {   // union entry `item`: its expert and its pairs (at most m, one per token)
         const PlanEntry pe = plan_entry(p.plan, p.topk_ids, p.m, p.top_k, p.n_experts, item);
         if (pe.e < 0) return;   // uniform: past this plan's union, or not a valid entry
         e = pe.e;

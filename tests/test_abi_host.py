@@ -264,3 +264,28 @@ def test_router_logits_refusals():
     assert L.ffnq_router_logits(x + 4, w, 2, 256, 8, lg, None) == -1          # misaligned
     assert L.ffnq_router_logits(x, w, 2, 256, 8, x + 16, None) == -1          # logits overlap x
     assert L.ffnq_router_logits(x, w, 0, 256, 8, lg, None) == 0               # m == 0: no-op
+
+
+def call_layer_logits(f, sh, E=8, hidden=256, inter=256, sh_inter=512, m=3, k=2, cap=8, plan_bytes=None,
+                      logits=addr(46), ws=None, ws_bytes=0):
+    L = fq.lib()
+    size = C.c_size_t(ws_bytes)
+    pb = 4 * fq.plan_ints(m, k) if plan_bytes is None else plan_bytes
+    rc = L.ffnq_moe_layer_logits(C.byref(f), E, hidden, inter, m, k, fq.ACT_SILU,
+                                 None if sh is None else C.byref(sh), sh_inter, addr(45), addr(40), logits, None, cap,
+                                 addr(41), addr(42), addr(43), pb, addr(50), ws, C.byref(size), None)
+    return rc, size.value
+
+
+def test_layer_logits_refusals_and_query():
+    # the checks of ffnq_moe_route and ffnq_moe_layer, and ffnq_moe_layer's workspace
+    f, sh = ffn(I4, I4, 256, 256), ffn(I4, I4, 256, 512)
+    rc, n = call_layer_logits(f, sh)
+    assert rc == 0 and n == call_layer(f, sh)[1]
+    assert call_layer_logits(f, sh, m=0) == (0, 0)
+    assert call_layer_logits(f, sh, logits=None)[0] == -1
+    assert call_layer_logits(f, sh, cap=33)[0] == -2
+    assert call_layer_logits(f, sh, k=4, cap=3)[0] == -3
+    assert call_layer_logits(f, sh, plan_bytes=4 * fq.plan_ints(3, 2) - 4)[0] == -4
+    assert call_layer_logits(ffn(I8, I4, 256, 256), sh)[0] == -2
+    assert call_layer_logits(f, sh, ws=addr(60), ws_bytes=n - 256)[0] == -4

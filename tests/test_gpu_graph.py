@@ -126,3 +126,47 @@ def test_graph_replay_moe_layer(tiled):
     want_o = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids_o, w_o, seed_o,
                                inp["resid"])
     check(host16(r), want_o, f"graph moe layer replay vs oracle tiled {tiled}")
+
+
+@LAYOUTS
+def test_graph_replay_moe_layer_logits(tiled):
+    # ffnq_moe_layer_logits (the router inside the gate/up launch when tiled)
+    # captured once and replayed; replays equal the eager call and the oracle
+    hidden, inter, E, m, k, cap, sh_inter = 512, 256, 32, 2, 8, 32, 384
+    say("graph moe layer logits", tiled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4646, shared_inter=sh_inter)
+    ex_d = mats_dev(inp["experts"], tiled, E)
+    ex = fq.ffn_struct(ex_d)
+    sh_d, sh = ffn_dev(inp["shared"], tiled)
+    x, r0, lg, gv = dev16(inp["x"]), dev16(inp["resid"]), dev(inp["logits"].astype(np.float32)), dev16(inp["gate_vec"])
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    ws = fq.Workspace()
+
+    def layer(resid):
+        fq.moe_layer_logits(ex, E, hidden, inter, m, k, gen.ACT_SILU, sh, sh_inter, gv, x, lg, cap, ids, w, plan,
+                            resid, ws=ws)
+
+    want = r0.clone()
+    layer(want)
+    torch.cuda.synchronize()
+    r = r0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(r)
+    for rep in range(4):
+        r.copy_(r0)
+        ids.fill_(-7)
+        plan.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r, want), rep
+    rc, ids_o, w_o, plan_o = oracle.moe_route(inp["logits"], k, cap)
+    assert rc == 0 and np.array_equal(ids.cpu().numpy(), ids_o) and np.array_equal(plan.cpu().numpy(), plan_o)
+    seed_o = oracle.shared_expert(inp["shared"], hidden, sh_inter, gen.ACT_SILU, gen.TAIL_SIGMOID_GATE, inp["x"],
+                                  inp["gate_vec"])
+    want_o = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids_o, w_o, seed_o,
+                               inp["resid"])
+    check(host16(r), want_o, f"graph moe layer logits replay vs oracle tiled {tiled}")

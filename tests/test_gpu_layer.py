@@ -118,3 +118,74 @@ def test_layer_without_shared_is_unseeded_routed(tiled):
     say("layer no shared", tiled)
     inp = gen.moe_inputs(hidden, E, inter, m, seed=4800)
     run_case(inp, E, hidden, inter, 0, m, k, cap, gen.ACT_SILU, tiled, tiled)
+
+
+# ---------------------------------------------------------------------------
+# ffnq_moe_layer_logits: route + layer in one call, bit for bit the two calls
+
+
+def logits_call(ex, sh, E, hidden, inter, sh_inter, m, k, cap, act, x, gate, logits, resid0, scale=None):
+    resid = resid0.clone()
+    ids = torch.full((m, k), -9, dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.full((fq.plan_ints(m, k),), -9, dtype=torch.int32, device="cuda")
+    fq.moe_layer_logits(ex, E, hidden, inter, m, k, act, sh, sh_inter, gate, x, logits, cap, ids, w, plan, resid,
+                        expert_scale=scale)
+    torch.cuda.synchronize()
+    return host16(resid), ids.cpu().numpy(), w.cpu().numpy(), plan.cpu().numpy()
+
+
+def route_then_layer(ex, sh, E, hidden, inter, sh_inter, m, k, cap, act, x, gate, logits, resid0, scale=None):
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    fq.moe_route(logits, m, E, k, cap, ids, w, plan, scale)
+    got = one_call(ex, sh, E, hidden, inter, sh_inter, m, k, act, x, gate, ids, w, plan, resid0)
+    return got, ids.cpu().numpy(), w.cpu().numpy(), plan.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,E,k,cap,sh_inter,tiled,scaled", [
+    (1, 16, 4, 8, 384, True, False),      # routed inside the gate/up launch
+    (3, 16, 4, 8, 384, True, False),      # several sub-batches
+    (4, 32, 8, 32, 384, True, True),      # expert scale
+    (2, 16, 4, 6, 0, True, False),        # no shared expert, a cap that splits
+    (4, 16, 4, 8, 384, False, False),     # row-major: the router runs first
+    (9, 16, 4, 8, 384, True, False),      # m > 4: the router runs first
+])
+def test_layer_logits_matches_route_then_layer(m, E, k, cap, sh_inter, tiled, scaled):
+    hidden, inter = 512, 256
+    say("layer logits small", m, E, k, cap, sh_inter, tiled, scaled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4900 + m + E + k, shared_inter=sh_inter)
+    ex_d, ex = mats(inp["experts"], tiled, E)
+    sh = None
+    if sh_inter:
+        sh_d, sh = mats(inp["shared"], tiled)
+    x, r0 = dev16(inp["x"]), dev16(inp["resid"])
+    gate = dev16(inp["gate_vec"]) if sh_inter else None
+    lg = dev(inp["logits"].astype(np.float32))
+    scale = dev((0.5 + np.random.default_rng(m).random(E)).astype(np.float32)) if scaled else None
+    a = logits_call(ex, sh, E, hidden, inter, sh_inter, m, k, cap, gen.ACT_SILU, x, gate, lg, r0, scale)
+    b = route_then_layer(ex, sh, E, hidden, inter, sh_inter, m, k, cap, gen.ACT_SILU, x, gate, lg, r0, scale)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    rc, ids_o, w_o, plan_o = oracle.moe_route(inp["logits"], k, cap,
+                                              None if scale is None else scale.cpu().numpy())
+    assert rc == 0 and np.array_equal(a[1], ids_o) and np.array_equal(a[3], plan_o)
+
+
+@pytest.mark.parametrize("c,m", [(3, 1), (3, 2), (3, 4), (4, 1), (4, 64)])
+def test_layer_logits_workloads(c, m):
+    cfg = gen.CONFIGS[c]
+    say("layer logits workload", c, m)
+    inp = gen.config_inputs(c, m)
+    hidden, E, inter, k = cfg["hidden"], cfg["n_experts"], cfg["moe_inter"], cfg["top_k"]
+    ex_d, ex = mats(inp["experts"], True, E)
+    sh, gate = None, None
+    if cfg["shared_inter"]:
+        sh_d, sh = mats(inp["shared"], True)
+        gate = dev16(inp["gate_vec"])
+    x, r0, lg = dev16(inp["x"]), dev16(inp["resid"]), dev(inp["logits"].astype(np.float32))
+    a = logits_call(ex, sh, E, hidden, inter, cfg["shared_inter"], m, k, cfg["cap"], cfg["act"], x, gate, lg, r0)
+    b = route_then_layer(ex, sh, E, hidden, inter, cfg["shared_inter"], m, k, cfg["cap"], cfg["act"], x, gate, lg, r0)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
