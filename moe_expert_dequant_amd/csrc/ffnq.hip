@@ -25,10 +25,12 @@ using namespace ffnq;
 
 constexpr size_t kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 constexpr size_t kLdsBig = 152 * 1024;     // one workgroup per CU (prefill-sized items)
+constexpr size_t kLdsMax = 160 * 1024;     // LDS of one gfx950 CU (one workgroup per CU)
 constexpr int kBigRows = 12;               // activation rows per item from which the prefill shapes apply
 
 // Rows per work item: every token (dense), or the pairs of one expert of the
-// union on average (routed; the union is at most min(pairs, experts)).
+// union on average (routed; an estimate: a plan of one sub-batch has at most
+// min(pairs, experts) union entries, one split by the slot cap may have more).
 int rows_per_item(bool dense, int m, int top_k, int n_experts)
 {
     if (dense) return m;
@@ -450,10 +452,11 @@ struct BurstCfg {
 };
 
 // gate/up: one K unit per wave, all of a tile's units in one workgroup.
-BurstCfg burst_gu_cfg(int fmt, int K, int N, int R)
+BurstCfg burst_gu_cfg(int fmt, int K, int N, int m)
 {
+    const int R = m <= 4 ? m : 8;   // activation rows of the kernel (rows past m repeat row 0)
     BurstCfg c{false, 1, R, 0};
-    if (!FFNQ_BURST || !is_tiled(fmt) || R < 1 || R > 4) return c;
+    if (!FFNQ_BURST || !is_tiled(fmt) || m < 1 || m > 8) return c;
     const int F = to_fmt(fmt);
     c.ks = burst_units(F, N, K);
     if (c.ks > 16) return c;
@@ -462,17 +465,21 @@ BurstCfg burst_gu_cfg(int fmt, int K, int N, int R)
     return c;
 }
 
-// down: up to 16 waves take the tile's K units in passes of one.
-BurstCfg burst_down_cfg(int fmt, int K, int N, int R)
+// down (m tokens: 2m hi/lo rows, R = 2, 4 or 8): the most waves, up to 16, whose
+// staging fits one CU's LDS take the tile's K units in passes of one.
+BurstCfg burst_down_cfg(int fmt, int K, int N, int m)
 {
+    const int R = m == 1 ? 2 : (m == 2 ? 4 : 8);
     BurstCfg c{false, 1, R, 0};
-    if (!FFNQ_BURST || !is_tiled(fmt) || R < 2 || R > 4) return c;
+    if (!FFNQ_BURST || !is_tiled(fmt) || m < 1 || m > 4) return c;
     const int F = to_fmt(fmt);
     const int nu = burst_units(F, N, K);
     if (nu > 64) return c;
-    c.ks = std::min(nu, 16);
-    c.lds = (size_t)burst_down_lds(F, R, c.ks, nu);
-    c.ok = c.lds <= kLdsBig;
+    for (c.ks = std::min(nu, 16); c.ks >= 1; --c.ks) {
+        c.lds = (size_t)burst_down_lds(F, R, c.ks, nu);
+        if (c.lds <= kLdsMax) break;
+    }
+    c.ok = c.ks >= 1 && (nu + c.ks - 1) / c.ks <= 4;   // at most four passes
     return c;
 }
 
@@ -483,8 +490,7 @@ BurstCfg dense_gu_burst(const ffnq_ffn* ffn, int hidden, int inter, int m)
 
 BurstCfg dense_down_burst(int fmt_down, int hidden, int inter, int m)
 {
-    if (m > 2) return BurstCfg{false, 1, 2 * m, 0};
-    return burst_down_cfg(fmt_down, inter, hidden, 2 * m);
+    return burst_down_cfg(fmt_down, inter, hidden, m);
 }
 
 #define FFNQ_GUB_CASE(F, R_)                                                                                  \
@@ -505,7 +511,8 @@ bool launch_gu_burst_jobs(int fmt, int R, int ks, size_t lds, const GUParams& a,
     if (!b) nb = 0;
     const int F_ = to_fmt(fmt);
     FFNQ_GUB_CASE(FMT_INT4, 1) FFNQ_GUB_CASE(FMT_INT4, 2) FFNQ_GUB_CASE(FMT_INT4, 3) FFNQ_GUB_CASE(FMT_INT4, 4)
-    FFNQ_GUB_CASE(FMT_INT8, 1) FFNQ_GUB_CASE(FMT_INT8, 2) FFNQ_GUB_CASE(FMT_INT8, 3) FFNQ_GUB_CASE(FMT_INT8, 4)
+    FFNQ_GUB_CASE(FMT_INT4, 8) FFNQ_GUB_CASE(FMT_INT8, 1) FFNQ_GUB_CASE(FMT_INT8, 2) FFNQ_GUB_CASE(FMT_INT8, 3)
+    FFNQ_GUB_CASE(FMT_INT8, 4) FFNQ_GUB_CASE(FMT_INT8, 8)
     return false;
 }
 
@@ -528,7 +535,8 @@ bool launch_down_burst(int fmt, const BurstCfg& c, int N, hipStream_t stream, co
     q.KG = 1;
     const int F_ = to_fmt(fmt);
     const int T = (N + 15) / 16;
-    FFNQ_DNB_CASE(FMT_INT4, 2) FFNQ_DNB_CASE(FMT_INT4, 4) FFNQ_DNB_CASE(FMT_INT8, 2) FFNQ_DNB_CASE(FMT_INT8, 4)
+    FFNQ_DNB_CASE(FMT_INT4, 2) FFNQ_DNB_CASE(FMT_INT4, 4) FFNQ_DNB_CASE(FMT_INT4, 8) FFNQ_DNB_CASE(FMT_INT8, 2)
+    FFNQ_DNB_CASE(FMT_INT8, 4) FFNQ_DNB_CASE(FMT_INT8, 8)
     return false;
 }
 
@@ -815,7 +823,6 @@ struct MoeDownCfg {
     size_t lds;
 };
 
-constexpr size_t kLdsMax = 160 * 1024;   // LDS of one gfx950 CU (one workgroup per CU)
 // Units a wave of moe_down_kernel stages per pass: one.  (Two per pass, with
 // both units' loads in flight together, gave NaN outputs on the Mixtral-shaped
 // layer -- 28 units per tile -- for a reason not yet found; that path is off.)
@@ -826,8 +833,8 @@ constexpr size_t kLdsMax = 160 * 1024;   // LDS of one gfx950 CU (one workgroup 
 MoeDownCfg moe_down_cfg(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
                         const ffnq_ffn* shared, int shared_inter)
 {
-    MoeDownCfg c{false, 2 * m, 1, 1, 0, 0};
-    if (!FFNQ_BURST || m > 2 || (long long)m * top_k > 64 || !is_tiled(experts->down.fmt) ||
+    MoeDownCfg c{false, m == 1 ? 2 : (m == 2 ? 4 : 8), 1, 1, 0, 0};
+    if (!FFNQ_BURST || m > 4 || (long long)m * top_k > 64 || !is_tiled(experts->down.fmt) ||
         !is_int4(experts->down.fmt))
         return c;
     int ns = 0;
@@ -837,7 +844,9 @@ MoeDownCfg moe_down_cfg(const ffnq_ffn* experts, int n_experts, int hidden, int 
         ns = burst_units(FMT_INT4, hidden, shared_inter);
     }
     const int nr = burst_units(FMT_INT4, hidden, moe_inter);
-    const long long umax = std::min<long long>((long long)m * top_k, n_experts);
+    // a plan's union has at most one entry per pair; it can hold more entries
+    // than there are experts when the slot cap splits the batch
+    const long long umax = (long long)m * top_k;
     const long long units = ns + umax * nr;
     if (units > 64) return c;
     c.max_units = (int)units;
@@ -873,7 +882,7 @@ bool launch_moe_down(const MoeDownCfg& c, int N, hipStream_t stream, const MoeDo
     MoeDownParams q = prm;
     q.ks = c.ks;
     q.max_units = c.max_units;
-    FFNQ_MDN_CASE(2, 1) FFNQ_MDN_CASE(4, 1)
+    FFNQ_MDN_CASE(2, 1) FFNQ_MDN_CASE(4, 1) FFNQ_MDN_CASE(8, 1)
     return false;
 }
 
@@ -990,7 +999,10 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
                               reinterpret_cast<float*>(sh->base + Ls.logit));
         sb = dense_gu_burst(sh->ffn, hidden, sh->inter, m);
     }
-    const int nr_items = (int)u_est * ((moe_inter + 15) / 16);
+    // burst workgroups: one per (union entry, tile) for every entry the plan can
+    // hold (one per pair; several sub-batches may repeat an expert), those past
+    // the plan's union return at once
+    const int nr_items = P * ((moe_inter + 15) / 16);
     if (rb.ok) {
         if (sh && sb.ok && to_fmt(sh->ffn->gate.fmt) == FMT_INT4 && sb.ks == rb.ks && sb.R == rb.R) {
             // shared and routed gate/up in one burst launch

@@ -49,10 +49,28 @@ __host__ __device__ inline int burst_wave_lds(int fmt, int nmat, int R, int upw)
     const int uin = fmt == FMT_INT4 ? 1024 : 512;
     return upw * (R * (uin * 2 + 64) + (fmt == FMT_INT4 ? nmat * 1024 : 0));
 }
-// A workgroup of ks waves, each one unit, meeting in a [ks][nmat][4][16] reduction.
+// Rows of a unit's sums kept in a reduction slot (R <= 8: MFMA rows 0-3 in
+// lanes 0-15, rows 4-7 in lanes 16-31, register i = row 4 * (lane / 16) + i).
+constexpr int kRedRows = 8;
+
+// A workgroup of ks waves, each one unit, meeting in a [ks][nmat][8][16] reduction.
 __host__ __device__ inline int burst_lds(int fmt, int nmat, int R, int upw, int ks)
 {
-    return ks * burst_wave_lds(fmt, nmat, R, upw) + ks * nmat * 4 * 16 * 4;
+    return ks * burst_wave_lds(fmt, nmat, R, upw) + ks * nmat * kRedRows * 16 * 4;
+}
+
+// Lanes 0..16*ceil(R/4)-1 hold a unit's sums: row 4 * (lane / 16) + i in
+// register i.  Writes them to slot[row][16] (rows < R).
+template <int R>
+__device__ __forceinline__ void burst_store_rows(float* slot, const float (&acc)[4])
+{
+    const int lane = threadIdx.x & 63;
+    if (lane < 16 * ((R + 3) / 4)) {
+        const int rb = 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < (R < 4 ? R : 4); ++i)
+            if (rb + i < R) slot[(rb + i) * 16 + (lane & 15)] = acc[i];
+    }
 }
 
 // One unit: tile `tile` of the matrices at tq (expert offset applied), K unit
@@ -63,11 +81,11 @@ struct BUnit {
     const uint8_t* tq[2];
     int n, k;                 // matrix rows and inputs
     int tile, u;
-    const uint16_t* row[4];
+    const uint16_t* row[8];
 };
 
-// UPW units of one wave; acc[uu][mt][i] = the unit's sum for rows i < R in
-// lanes 0-15 (lane = tile row).  INT4 applies the group scales; INT8 returns
+// UPW units of one wave; acc[uu][mt][i] = the unit's sum for row
+// 4 * (lane / 16) + i, tile row lane % 16 (rows < R, at most 8).  INT4 applies the group scales; INT8 returns
 // the unscaled sum of q*x (the code bias removed block by block; the row
 // scale is applied by the caller).  The first nvalid (uniform) units are
 // real; the code loads of the others repeat unit 0's, so that the number of
@@ -165,7 +183,8 @@ __device__ __forceinline__ void burst_wave(const BUnit (&un)[UPW], int nvalid, u
                         const float sg = jg ? bf16hi_f32(sz[0]) : bf16lo_f32(sz[0]);
                         const float zg = (jg ? bf16hi_f32(sz[1]) : bf16lo_f32(sz[1])) + 128.0f;
 #pragma unroll
-                        for (int i = 0; i < R; ++i) acc[uu][mt][i] = fmaf(sg, fmaf(-zg, o[jg][i], m[i]), acc[uu][mt][i]);
+                        for (int i = 0; i < (R < 4 ? R : 4); ++i)
+                            acc[uu][mt][i] = fmaf(sg, fmaf(-zg, o[jg][i], m[i]), acc[uu][mt][i]);
                     }
                 }
             } else {
@@ -182,7 +201,7 @@ __device__ __forceinline__ void burst_wave(const BUnit (&un)[UPW], int nvalid, u
                         m = mfma_bf16(xs[d], u32x4{p0[0], p0[1], p1[0], p1[1]}, m);
                     }
 #pragma unroll
-                    for (int i = 0; i < R; ++i) acc[uu][mt][i] += fmaf(-128.0f, o[i], m[i]);
+                    for (int i = 0; i < (R < 4 ? R : 4); ++i) acc[uu][mt][i] += fmaf(-128.0f, o[i], m[i]);
                 }
             }
         }
@@ -323,21 +342,17 @@ __device__ __forceinline__ void gu_burst_job(const GUParams& p, int bx)
     const int wlds = burst_wave_lds(FMT, 2, R, 1);
     float acc[1][2][4];
     burst_wave<FMT, 2, R, 1>(un, 1, smem + w * wlds, acc);
-    float* red = (float*)(smem + p.ks * wlds);   // [ks][2][4][16]
-    if (lane < 16) {
+    float* red = (float*)(smem + p.ks * wlds);   // [ks][2][8][16]
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < R; ++i) red[((w * 2 + mt) * 4 + i) * 16 + lane] = acc[0][mt][i];
-    }
+    for (int mt = 0; mt < 2; ++mt) burst_store_rows<R>(red + (w * 2 + mt) * kRedRows * 16, acc[0][mt]);
     __syncthreads();
-    if (tid < rows * 16) {
-        const int i = tid >> 4, nl = tid & 15, n = tile * 16 + nl;
+    for (int ti = tid; ti < rows * 16; ti += blockDim.x) {   // rows * 16 may exceed one wave's lanes
+        const int i = ti >> 4, nl = ti & 15, n = tile * 16 + nl;
         float v[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             float h = 0.f;
-            for (int ww = 0; ww < p.ks; ++ww) h += red[((ww * 2 + mt) * 4 + i) * 16 + nl];
+            for (int ww = 0; ww < p.ks; ++ww) h += red[((ww * 2 + mt) * kRedRows + i) * 16 + nl];
             v[mt] = h * burst_row_scale<FMT>(un[0].tq[mt], n, p.N, p.K);
         }
         const int orow = routed ? nth_bit(pairs, i) : i;
@@ -381,7 +396,7 @@ __global__ void __launch_bounds__(1024) gu_burst_kernel(GUParams a, GUParams b, 
 // added (hi + lo, as the streaming kernels do), scaled (INT8) and finished.
 __host__ __device__ inline int burst_down_lds(int fmt, int R, int ks, int units)
 {
-    return ks * burst_wave_lds(fmt, 1, R, 1) + units * 4 * 16 * 4;
+    return ks * burst_wave_lds(fmt, 1, R, 1) + units * kRedRows * 16 * 4;
 }
 
 template <int FMT, int R>
@@ -389,11 +404,11 @@ __global__ void __launch_bounds__(1024) down_burst_kernel(DownParams p)
 {
     static_assert(R % 2 == 0, "hi/lo row pairs");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int w = uniform(threadIdx.x >> 6), tid = threadIdx.x;
     const int tile = blockIdx.x;
     const int nu = burst_units(FMT, p.N, p.K);
     const int wlds = burst_wave_lds(FMT, 1, R, 1);
-    float* red = (float*)(smem + p.ks * wlds);   // [nu][4][16]
+    float* red = (float*)(smem + p.ks * wlds);   // [nu][8][16]
     for (int q = w; q < nu; q += p.ks) {
         BUnit un[1];
         un[0].tq[0] = p.tdown;
@@ -403,21 +418,18 @@ __global__ void __launch_bounds__(1024) down_burst_kernel(DownParams p)
         un[0].tile = tile;
         un[0].u = q;
 #pragma unroll
-        for (int r = 0; r < R; ++r) un[0].row[r] = p.act + (size_t)r * p.K;
+        for (int r = 0; r < R; ++r) un[0].row[r] = p.act + (size_t)min(r, 2 * p.m - 1) * p.K;
         float acc[1][1][4];
         burst_wave<FMT, 1, R, 1>(un, 1, smem + w * wlds, acc);
-        if (lane < 16) {
-#pragma unroll
-            for (int i = 0; i < R; ++i) red[(q * 4 + i) * 16 + lane] = acc[0][0][i];
-        }
+        burst_store_rows<R>(red + q * kRedRows * 16, acc[0][0]);
     }
     __syncthreads();
-    if (tid < (R / 2) * 16) {
+    if (tid < p.m * 16) {
         const int t = tid >> 4, nl = tid & 15, n = tile * 16 + nl;
         float hh = 0.f, hl = 0.f;
         for (int q = 0; q < nu; ++q) {
-            hh += red[(q * 4 + 2 * t) * 16 + nl];
-            hl += red[(q * 4 + 2 * t + 1) * 16 + nl];
+            hh += red[(q * kRedRows + 2 * t) * 16 + nl];
+            hl += red[(q * kRedRows + 2 * t + 1) * 16 + nl];
         }
         const float h = (hh + hl) * burst_row_scale<FMT>(p.tdown, n, p.N, p.K);
         if (n < p.N) down_finish(p, 0, t, n, h);
@@ -466,7 +478,7 @@ struct MoeDownParams {
 // reduction slots, and the pair table (entry, place, weight; 64 pairs).
 __host__ __device__ inline int moe_down_lds(int fmt, int R, int upp, int ks, int max_units)
 {
-    return ks * burst_wave_lds(fmt, 1, R, upp) + max_units * 4 * 16 * 4 + 64 * 12;
+    return ks * burst_wave_lds(fmt, 1, R, upp) + max_units * kRedRows * 16 * 4 + 64 * 12;
 }
 
 template <int FMT, int R, int UPP>
@@ -481,8 +493,8 @@ __global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
     const int nr = burst_units(FMT, p.N, p.K);
     const int Q = p.max_units;     // ns + nr * (largest possible union)
     const int wlds = burst_wave_lds(FMT, 1, R, UPP);
-    float* red = (float*)(smem + p.ks * wlds);         // [Q][4][16]
-    int* tg = (int*)(red + (size_t)Q * 4 * 16);        // per pair: union entry (-1: adds nothing)
+    float* red = (float*)(smem + p.ks * wlds);         // [Q][8][16]
+    int* tg = (int*)(red + (size_t)Q * kRedRows * 16); // per pair: union entry (-1: adds nothing)
     int* tj = tg + 64;                                 // its place among the entry's pairs
     float* tw = (float*)(tj + 64);                     // its route weight
 
@@ -529,14 +541,9 @@ __global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
         if (nvalid == 0) break;   // uniform: the rest of this wave's units are past the union
         float acc[UPP][1][4];
         burst_wave<FMT, 1, R, UPP>(un, nvalid, smem + w * wlds, acc);
-        if (lane < 16) {
 #pragma unroll
-            for (int uu = 0; uu < UPP; ++uu)
-                if (uu < nvalid) {
-#pragma unroll
-                    for (int i = 0; i < R; ++i) red[(qs[uu] * 4 + i) * 16 + lane] = acc[uu][0][i];
-                }
-        }
+        for (int uu = 0; uu < UPP; ++uu)
+            if (uu < nvalid) burst_store_rows<R>(red + qs[uu] * kRedRows * 16, acc[uu][0]);
     }
     // the pair table, by wave 0 (one lane per pair): entry g of pair p is the
     // entry of its token's sub-batch whose expert is the pair's; its place is
@@ -590,8 +597,8 @@ __global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
     auto pair_sum = [&](int q0, int nu, int j) {
         float hh = 0.f, hl = 0.f;
         for (int q = q0; q < q0 + nu; ++q) {
-            hh += red[(q * 4 + 2 * j) * 16 + nl];
-            hl += red[(q * 4 + 2 * j + 1) * 16 + nl];
+            hh += red[(q * kRedRows + 2 * j) * 16 + nl];
+            hl += red[(q * kRedRows + 2 * j + 1) * 16 + nl];
         }
         return hh + hl;
     };

@@ -102,6 +102,7 @@ def test_layer_config3_matches_two_calls(m):
     (3, 2, 8, False, False, gen.FMT_INT4_AFFINE_G64),   # row-major: separate launches
     (4, 4, 8, True, False, gen.FMT_INT8_ROW),           # INT8 row-major shared expert, tiled experts
     (20, 2, 16, True, True, gen.FMT_INT4_AFFINE_G64),   # more rows per expert
+    (8, 8, 16, True, True, gen.FMT_INT4_AFFINE_G64),    # 64 pairs: eight activation rows per burst unit
 ])
 def test_layer_small_matches_two_calls(m, k, cap, tiled_ex, sh_tiled, sh_fmt):
     hidden, inter, E, sh_inter = 512, 256, 16, 384
@@ -110,6 +111,19 @@ def test_layer_small_matches_two_calls(m, k, cap, tiled_ex, sh_tiled, sh_fmt):
     inp["shared"] = gen.ffn(sh_fmt, sh_fmt, hidden, sh_inter, gen.tensor_key(4700 + m, 1))
     inp["gate_vec"] = gen.gate_vector(gen.tensor_key(4701 + m, 2), hidden)
     run_case(inp, E, hidden, inter, sh_inter, m, k, cap, gen.ACT_SILU, tiled_ex, sh_tiled)
+
+
+@pytest.mark.parametrize("m,E,k,cap", [(3, 8, 4, 4), (4, 8, 4, 5)])
+def test_layer_union_past_experts(m, E, k, cap):
+    # sub-batches whose union entries outnumber the experts, through the fused down
+    hidden, inter, sh_inter = 512, 256, 384
+    say("layer union past experts", m, E, k, cap)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4650 + m + E, shared_inter=sh_inter)
+    rc, _, _, plan_o = oracle.moe_route(inp["logits"], k, cap)
+    assert rc == 0 and plan_o[m + 2 + plan_o[0]] > E
+    got, seed, ids, w = run_case(inp, E, hidden, inter, sh_inter, m, k, cap, gen.ACT_SILU, True, True)
+    want = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids, w, seed, inp["resid"])
+    assert rel_l2_rows(got, want) <= TOL
 
 
 @pytest.mark.parametrize("tiled", [False, True])

@@ -343,6 +343,24 @@ def test_routed_small(m, k, cap, use_seed, tiled):
     check(got, want, f"routed m {m} k {k} cap {cap} seed {use_seed}")
 
 
+@LAYOUTS
+@pytest.mark.parametrize("m,E,k,cap", [(3, 8, 4, 4), (4, 8, 4, 4), (8, 16, 8, 8)])
+def test_routed_union_past_experts(m, E, k, cap, tiled):
+    # a slot cap below the batch's union splits it into sub-batches whose
+    # union entries, together, outnumber the experts: every entry must run
+    hidden, inter = 512, 256
+    say("routed union past experts", m, E, k, cap, tiled)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=3200 + m + E + k)
+    rc, _, _, plan_o = oracle.moe_route(inp["logits"], k, cap)
+    assert rc == 0 and plan_o[m + 2 + plan_o[0]] > E   # the case this test is for
+    seed_bits = gen.act_rows(gen.tensor_key(3201, m), m, hidden)
+    d = mats_dev(inp["experts"], tiled, E)
+    got, ids, w = gpu_routed(d, fq.ffn_struct(d), E, hidden, inter, k, cap, inp, seed_bits)
+    want = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids, w, seed_bits,
+                             inp["resid"])
+    check(got, want, f"routed union past experts m {m} E {E} k {k} cap {cap}")
+
+
 # ---------------------------------------------------------------------------
 # prefill-sized routed items (12 or more rows per expert), reduced width, every row
 
