@@ -41,9 +41,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 KERNEL_SOURCES = tuple(f"moe_expert_dequant_amd/csrc/{f}" for f in
-                       ("device.h", "qgemm.h", "tiled.h", "route.h", "tail.h", "ffnq.hip"))
-TRAFFIC_FILE = "profiles/traffic_gu_tiled_kernel_int4_llama3-8b_m1.txt"
+                       ("device.h", "qgemm.h", "tiled.h", "route.h", "stream.h", "tail.h", "ffnq.hip"))
+TRAFFIC_FILE = "profiles/traffic_gu_burst_kernel_int4_llama3-8b_m1.txt"
 
 
 def weight_bytes(fmt: int, n: int, k: int) -> int:
@@ -238,6 +239,8 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
         bytes_of = lambda: wbytes + io
     else:
         E, inter, k, cap = cfg["n_experts"], cfg["moe_inter"], cfg["top_k"], cfg["cap"]
+        sandwich = cfg["kind"] == "sandwich"
+        sh_fmt = cfg.get("shared_fmt", cfg["fmt"])
         ex = {n: fq.pack(fq.to_device(inp["experts"][n]), E) for n in ("gate", "up", "down")}
         ebytes = 2 * weight_bytes(cfg["fmt"], inter, hidden) + weight_bytes(cfg["fmt"], hidden, inter)
         sh = None
@@ -247,32 +250,48 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
         ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
         w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
         plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
-        fq.moe_route(logits, m, E, k, cap, ids, w, plan)
+        escale = torch.from_numpy(inp["expert_scale"]).cuda() if sandwich else None
+        fq.moe_route(logits, m, E, k, cap, ids, w, plan, escale)
         torch.cuda.synchronize()
         p = plan.cpu().numpy()
         n_sub = min(max(int(p[0]), 0), m)
         union = min(max(int(p[m + 2 + n_sub]), 0), m * k)           # union entries of all sub-batches
-        touched = union * ebytes + (0 if sh is None else 2 * weight_bytes(cfg["fmt"], cfg["shared_inter"], hidden)
-                                    + weight_bytes(cfg["fmt"], hidden, cfg["shared_inter"]))
+        touched = union * ebytes + (0 if sh is None else 2 * weight_bytes(sh_fmt, cfg["shared_inter"], hidden)
+                                    + weight_bytes(sh_fmt, hidden, cfg["shared_inter"]))
         copies = max(2, -(-2 * 256 * 1000 * 1000 // max(touched, 1)))
         exs = [ex] + [_clone_mats(ex) for _ in range(copies - 1)]
         ex_st = [fq.ffn_struct(d) for d in exs]
-        shs = None if sh is None else [fq.ffn_struct(d) for d in ([sh] + [_clone_mats(sh) for _ in range(copies - 1)])]
-        gv = _dev16(inp["gate_vec"]) if sh is not None else None
+        # the copies' tensors stay referenced for as long as their structs are used (a struct holds raw pointers)
+        sh_copies = None if sh is None else [sh] + [_clone_mats(sh) for _ in range(copies - 1)]
+        shs = None if sh is None else [fq.ffn_struct(d) for d in sh_copies]
+        gv = _dev16(inp["gate_vec"]) if (sh is not None and not sandwich) else None
 
-        def call(i):   # router top-k + plan, the gated shared expert and the routed half: one call
-            fq.moe_layer_logits(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"],
-                                None if shs is None else shs[i % copies], cfg["shared_inter"] or 0, gv, x, logits,
-                                cap, ids, w, plan, resid, ws=ws)
+        if sandwich:
+            n1, n2 = _dev16(inp["shared_norm_w"]), _dev16(inp["post_norm_w"])
+
+            def call(i):   # route (expert scale), shared branch + its norm, unseeded routed half, sandwich tail
+                fq.moe_layer_sandwich(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"], shs[i % copies],
+                                      cfg["shared_inter"], n1, n2, cfg["eps"], x, logits, cap, ids, w, plan, resid,
+                                      expert_scale=escale, ws=ws)
+        else:
+            def call(i):   # router top-k + plan, the gated shared expert and the routed half: one call
+                fq.moe_layer_logits(ex_st[i % copies], E, hidden, inter, m, k, cfg["act"],
+                                    None if shs is None else shs[i % copies], cfg["shared_inter"] or 0, gv, x,
+                                    logits, cap, ids, w, plan, resid, ws=ws)
         counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
         extra = dict(union=union, sub_batches=n_sub, tokens_per_expert_min=int(counts[counts > 0].min()),
                      tokens_per_expert_max=int(counts.max()))
         extra["router_gemv_us"] = time_router_gemv(x, m, hidden, E)
         io = 2 * m * hidden + 4 * m * E + 4 * m * hidden                 # x; logits; residual read and written
+        if sandwich:
+            io += 4 * hidden + 4 * E                                     # the two norm weights; the expert scale
         bytes_of = lambda: touched + io
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
+    # per-kernel figures for the layers whose gate/up and down each run in one launch
+    phases = kernel_phases(c, m, cfg, call, min(steps, 50), extra.get("union")) if cfg["kind"] != "sandwich" else []
+    graph_us = graph_call_us(call, max(copies, 8), steps)
     st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
@@ -285,7 +304,94 @@ def run_config(c: int, m: int, steps: int, warmup: int) -> dict:
     nb = bytes_of()
     return dict(call_us_median=med * 1e6, call_us_p10=float(np.percentile(t, 10)) * 1e6,
                 call_us_p90=float(np.percentile(t, 90)) * 1e6, tokens_per_s=m / med, bytes_per_call=nb,
-                achieved_GBs=nb / med / 1e9, frac_of_peak=nb / med / 1e9 / HBM_PEAK_GBS, weight_copies=copies, **extra)
+                achieved_GBs=nb / med / 1e9, frac_of_peak=nb / med / 1e9 / HBM_PEAK_GBS, weight_copies=copies,
+                graph_call_us=graph_us, graph_tokens_per_s=m / (graph_us * 1e-6),
+                graph_frac_of_peak=nb / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS, kernels=phases, **extra)
+
+
+# The kernels the library launches for the gate/up and down phases of each
+# workload shape (its dispatch at these sizes; the rocprofv3 kernel traces
+# under profiles/ list the same names).
+def kernel_names(c: int, m: int):
+    dense_gu = {0: "INT8", 1: "INT4", 2: "INT8"}
+    if c in dense_gu:
+        f = dense_gu[c]
+        r_gu = m if m <= 4 else 8
+        down = f"down_burst_kernel<{f},{2 * m if m <= 2 else 8}>" if m <= 4 else f"down_tiled_kernel<{f},...>"
+        return f"gu_burst_kernel<{f},{r_gu}>", down
+    if c == 3:
+        return (f"gu_burst_kernel<INT4,{m}> (shared + routed gate/up{', routing' if m * 128 <= 128 else ''})",
+                f"moe_down_kernel<INT4,{2 * m if m <= 2 else 8},1> (shared + routed down, seeded reduce, residual)")
+    if m == 1:
+        return ("gu_burst_kernel<INT4,1> (routed gate/up, routing)",
+                "moe_down_kernel<INT4,2,1> (routed down, reduce, residual)")
+    return "gu_tiled_kernel<INT4,...> (grouped bf16-MFMA gate/up)", "down_tiled_kernel<INT4,...> (grouped down)"
+
+
+def kernel_phases(c: int, m: int, cfg: dict, call, n: int, union) -> list:
+    """Average duration of the gate/up and of the down launch of one call (HIP
+    events that the library attaches to those kernel dispatches) and each
+    one's algorithmic bytes: the weights it must read (the union's experts for
+    a routed layer), x for gate/up, the residual read and write when the tail
+    runs in the down kernel.  FLOPs are 2 per weight per token (per pair)."""
+    import torch
+    import moe_expert_dequant_amd as fq
+
+    hidden, fmt = cfg["hidden"], cfg["fmt"]
+    if cfg["kind"] in ("dense", "shared"):
+        inter = cfg["inter"]
+        gu_b = 2 * weight_bytes(fmt, inter, hidden) + 2 * m * hidden
+        dn_b = weight_bytes(fmt, hidden, inter) + (4 * m * hidden if cfg["kind"] == "dense" else 0)
+        gu_f, dn_f = 2 * m * 2 * inter * hidden, 2 * m * hidden * inter
+    else:
+        inter, k, si = cfg["moe_inter"], cfg["top_k"], cfg["shared_inter"] or 0
+        gu_b = union * 2 * weight_bytes(fmt, inter, hidden) + 2 * m * hidden
+        dn_b = union * weight_bytes(fmt, hidden, inter) + 4 * m * hidden
+        gu_f, dn_f = 2 * m * k * 2 * inter * hidden, 2 * m * k * hidden * inter
+        if si:
+            gu_b += 2 * weight_bytes(fmt, si, hidden) + 2 * hidden      # shared gate/up; its gate vector
+            dn_b += weight_bytes(fmt, hidden, si)
+            gu_f += 2 * m * 2 * si * hidden
+            dn_f += 2 * m * hidden * si
+    evs = [fq.PhaseEvents() for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        with evs[i]:
+            call(i)
+    torch.cuda.synchronize()
+    d = np.array([e.durations() for e in evs]).mean(axis=0) * 1e-3   # s: gate/up, down
+    names = kernel_names(c, m)
+    out = []
+    for name, phase, b, f, t in ((names[0], "gate_up", gu_b, gu_f, d[0]), (names[1], "down", dn_b, dn_f, d[1])):
+        gbs = b / t / 1e9
+        e = dict(workload=cfg["name"], m=m, phase=phase, kernel=name, bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS,
+                 unit="GB/s", frac=gbs / HBM_PEAK_GBS, algorithmic_bytes_per_launch=b, avg_launch_us=t * 1e6,
+                 flops_per_launch=f, tflops=f / t / 1e12)
+        if m * (cfg.get("top_k") or 1) >= 64:   # the grouped prefill GEMMs run on bf16 MFMA
+            e["mfma_frac"] = f / t / 1e12 / BF16_MFMA_PEAK_TFLOPS
+        out.append(e)
+    return out
+
+
+def graph_call_us(call, ncalls: int, steps: int) -> float:
+    """Per-call time of `ncalls` calls captured in one HIP graph and replayed
+    (the launches of a layer without the host's per-launch cost)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(ncalls):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, steps // ncalls)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * ncalls)
 
 
 def time_router_gemv(x, m: int, hidden: int, E: int, calls: int = 50) -> float:
@@ -501,8 +607,8 @@ def main():
         traffic = read_traffic() if args.m == 1 else None
         out["roofline"] = {
             "bound": "hbm",
-            "kernel": ("gu_kernel" if args.rowmajor else "gu_tiled_kernel") +
-                      "<INT4,1,1> (gate+up dequant GEMV + SiLU gate-multiply)",
+            "kernel": ("gu_kernel<INT4,...>" if args.rowmajor else f"gu_burst_kernel<INT4,{args.m if args.m <= 4 else 8}>") +
+                      " (gate+up dequant GEMV + SiLU gate-multiply)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -521,6 +627,8 @@ def main():
                     for m, r in res.items()}
     if not (args.no_configs or args.single):
         out["configs"] = run_configs(100, 10)
+        # every workload shape's gate/up and down kernels against their roofline
+        out["roofline_kernels"] = [k for cf in out["configs"].values() for r in cf.values() for k in r["kernels"]]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -190,6 +190,12 @@ CONFIGS = {
             shared_inter=5632, fmt=FMT_INT4_AFFINE_G64, act=ACT_SILU, cap=32, ms=(1, 2, 4)),
     4: dict(name="mixtral-8x7b-int4", kind="moe", hidden=4096, n_experts=8, moe_inter=14336, top_k=2,
             shared_inter=0, fmt=FMT_INT4_AFFINE_G64, act=ACT_SILU, cap=32, ms=(1, 64)),
+    # the Gemma-style routed layer (sandwich tail): the shared branch is workload
+    # 2's INT8 FFN with its RMSNorm; the routed experts' shape (128 experts, top 8,
+    # 768 wide, INT4) is this generator's own choice -- the pages give none
+    5: dict(name="gemma-style-moe-sandwich", kind="sandwich", hidden=2816, n_experts=128, moe_inter=768, top_k=8,
+            shared_inter=11264, shared_fmt=FMT_INT8_ROW, fmt=FMT_INT4_AFFINE_G64, act=ACT_GELU_TANH, eps=1e-6,
+            cap=32, ms=(1, 4)),
 }
 
 
@@ -221,12 +227,28 @@ def moe_inputs(hidden: int, n_experts: int, moe_inter: int, m: int, seed: int,
     return d
 
 
+def sandwich_inputs(hidden: int, n_experts: int, moe_inter: int, m: int, seed: int, shared_inter: int,
+                    shared_fmt: int = FMT_INT8_ROW, fmt: int = FMT_INT4_AFFINE_G64, row_scales: bool = False) -> dict:
+    """The Gemma-style routed layer: moe_inputs' experts, x, residual and logits, a
+    shared FFN, the two norm weights and a per-expert router scale U(0.5, 1.5)."""
+    d = moe_inputs(hidden, n_experts, moe_inter, m, seed, 0, fmt)
+    d["shared"] = ffn(shared_fmt, shared_fmt, hidden, shared_inter, tensor_key(seed, 204), row_scales=row_scales)
+    d["shared_norm_w"] = norm_weight(tensor_key(seed, 206), hidden)
+    d["post_norm_w"] = norm_weight(tensor_key(seed, 207), hidden)
+    d["expert_scale"] = (0.5 + uniform(tensor_key(seed, 208), n_experts)).astype(np.float32)
+    return d
+
+
 def config_inputs(c: int, m: int, row_scales: bool = False) -> dict:
     """Inputs of workload c at m tokens; the seed of workload c is c.  row_scales
     replaces the INT8 workloads' constant row scale by per-row draws (qmat)."""
     cfg = CONFIGS[c]
     if cfg["kind"] in ("dense", "shared"):
         return dense_inputs(cfg["hidden"], cfg["inter"], m, cfg["fmt"], seed=c, row_scales=row_scales)
+    if cfg["kind"] == "sandwich":
+        return sandwich_inputs(cfg["hidden"], cfg["n_experts"], cfg["moe_inter"], m, seed=c,
+                               shared_inter=cfg["shared_inter"], shared_fmt=cfg["shared_fmt"], fmt=cfg["fmt"],
+                               row_scales=row_scales)
     return moe_inputs(cfg["hidden"], cfg["n_experts"], cfg["moe_inter"], m, seed=c,
                       shared_inter=cfg["shared_inter"], fmt=cfg["fmt"])
 

@@ -333,7 +333,7 @@ FFNQ_API int ffnq_moe_layer(const ffnq_ffn* experts, int n_experts, int hidden, 
  * then the gated shared expert and the routed half), with the same results
  * bit for bit: topk_ids, topk_w and plan are written as ffnq_moe_route writes
  * them, and resid as ffnq_moe_layer leaves it.  For small batches (tiled INT4
- * experts, m <= 4, at most 64 pairs and m * n_experts <= 128 keys) the routing
+ * experts, m <= 8, at most 64 pairs and m * n_experts <= 128 keys) the routing
  * runs inside the routed gate/up launch, every workgroup of which repeats it,
  * so the layer has no separate router launch; otherwise the router runs first
  * on the same stream.
@@ -347,6 +347,44 @@ FFNQ_API int ffnq_moe_layer_logits(const ffnq_ffn* experts, int n_experts, int h
                                    const float* expert_scale, int slot_cap, int32_t* topk_ids, float* topk_w,
                                    int32_t* plan, size_t plan_bytes, uint16_t* resid, void* ws, size_t* ws_bytes,
                                    hipStream_t stream);
+
+/* ---- ffnq_moe_layer_sandwich -----------------------------------------------
+ * The Gemma-style routed layer ([qwen/moe_batch.rs] module doc, first bullet:
+ * Gemma's routed sum starts from nothing and its shared branch joins in the
+ * sandwich tail after a norm; the router takes a learned per-expert scale;
+ * [gemma4/shared_expert.rs] `encode_shared_expert_branch`: the shared branch's
+ * down projection, then `post_feedforward_layernorm_1` into the bf16 row h1).
+ * Per token t:
+ *     route:   topk_ids, topk_w, plan as ffnq_moe_route(logits, expert_scale,
+ *              ..., slot_cap) writes them;
+ *     h1_t   = the shared expert with the RMSNorm tail (shared_norm_w, eps),
+ *              bit for bit ffnq_shared_expert(..., FFNQ_TAIL_RMSNORM, ...);
+ *     r_t    = bf16 of the routed sum started at +0.0 (no seed), bit for bit
+ *              ffnq_moe_routed_batched(..., seed = NULL) on a zero row;
+ *     z      = h1_t + r_t (exact), n = bf16(z / sqrt(mean(z^2) + eps) *
+ *              post_norm_w), resid_t = bf16(resid_t + n).
+ * The pages give no more of the sandwich tail than that the shared branch
+ * joins after its own norm; the join, the second norm over it and the final
+ * residual add are this library's reading of that sentence.
+ * experts:        tiled or row-major INT4-affine g64 experts (UNSUPPORTED
+ *                 otherwise), as for ffnq_moe_routed_batched.
+ * shared:         the shared expert (any supported format; required).
+ * shared_norm_w:  device bf16 [hidden], the shared branch's norm weight.
+ * post_norm_w:    device bf16 [hidden], the tail norm's weight.
+ * eps:            both norms' epsilon (finite, >= 0).
+ * logits, expert_scale, slot_cap, topk_ids, topk_w, plan, plan_bytes: as for
+ *                 ffnq_moe_route (outputs here).
+ * x, resid:       as for ffnq_moe_routed_batched.
+ * Workspace: h1 and r, the shared expert's workspace and the routed half's;
+ * ws == NULL returns the size.  Errors: those of the calls it composes.
+ */
+FFNQ_API int ffnq_moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m,
+                                     int top_k, int act, const ffnq_ffn* shared, int shared_inter,
+                                     const uint16_t* shared_norm_w, const uint16_t* post_norm_w, float eps,
+                                     const uint16_t* x, const float* logits, const float* expert_scale,
+                                     int slot_cap, int32_t* topk_ids, float* topk_w, int32_t* plan,
+                                     size_t plan_bytes, uint16_t* resid, void* ws, size_t* ws_bytes,
+                                     hipStream_t stream);
 
 /* ---- ffnq_packed_bytes / ffnq_pack -----------------------------------------
  * Bytes of one n x k matrix (one expert) in a tiled format; fmt may name the

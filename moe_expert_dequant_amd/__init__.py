@@ -31,7 +31,7 @@ OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
 EXPORTS = ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
            "ffnq_moe_routed_batched",
-           "ffnq_moe_layer", "ffnq_moe_layer_logits",
+           "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich",
            "ffnq_status_string", "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
 
 
@@ -76,9 +76,11 @@ def lib():
         L.ffnq_moe_layer.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ffnq_moe_layer_logits.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, vp, vp, i32, vp, vp, vp,
                                             C.c_size_t, vp, vp, sz, vp]
+        L.ffnq_moe_layer_sandwich.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, f32, vp, vp, vp,
+                                              i32, vp, vp, vp, C.c_size_t, vp, vp, sz, vp]
         for f in ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
                   "ffnq_moe_routed_batched",
-                  "ffnq_moe_layer", "ffnq_moe_layer_logits"):
+                  "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich"):
             getattr(L, f).restype = C.c_int
         L.ffnq_status_string.argtypes = [C.c_int]
         L.ffnq_status_string.restype = C.c_char_p
@@ -249,6 +251,21 @@ def moe_layer_logits(experts: Ffn, n_experts: int, hidden: int, moe_inter: int, 
             _ptr(expert_scale), slot_cap, _ptr(topk_ids), _ptr(topk_w), _ptr(plan), nbytes, _ptr(resid))
     buf, n = _ws(L.ffnq_moe_layer_logits, args, ws)
     _check("ffnq_moe_layer_logits", L.ffnq_moe_layer_logits(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+def moe_layer_sandwich(experts: Ffn, n_experts: int, hidden: int, moe_inter: int, m: int, top_k: int, act: int,
+                       shared: Ffn, shared_inter: int, shared_norm_w, post_norm_w, eps: float, x, logits,
+                       slot_cap: int, topk_ids, topk_w, plan, resid, expert_scale=None, ws: Workspace | None = None,
+                       stream=None):
+    """ffnq_moe_layer_sandwich: the Gemma-style routed layer (route with the per-expert scale, the shared branch
+    with its RMSNorm tail, the unseeded routed sum, the sandwich tail) in one call."""
+    L = lib()
+    nbytes = plan.numel() * plan.element_size()
+    args = (C.byref(experts), n_experts, hidden, moe_inter, m, top_k, act, C.byref(shared), shared_inter,
+            _ptr(shared_norm_w), _ptr(post_norm_w), eps, _ptr(x), _ptr(logits), _ptr(expert_scale), slot_cap,
+            _ptr(topk_ids), _ptr(topk_w), _ptr(plan), nbytes, _ptr(resid))
+    buf, n = _ws(L.ffnq_moe_layer_sandwich, args, ws)
+    _check("ffnq_moe_layer_sandwich", L.ffnq_moe_layer_sandwich(*args, _ptr(buf), C.byref(n), _stream(stream)))
 
 
 def workspace_bytes(kind: str, *args) -> int:

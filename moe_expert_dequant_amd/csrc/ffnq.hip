@@ -1247,6 +1247,89 @@ int moe_layer_common(const ffnq_ffn* experts, int n_experts, int hidden, int moe
 }
 
 // ---------------------------------------------------------------------------
+// The Gemma-style routed layer (ffnq_moe_layer_sandwich): route with the
+// per-expert scale; the shared branch with its own RMSNorm tail into the bf16
+// row h1; the routed half unseeded into the bf16 row r (the routed call on a
+// zeroed row: its sum starts from nothing); the sandwich tail.  Workspace:
+// h1 and r, then the shared branch's workspace, then the routed half's.
+struct SandwichWs {
+    size_t h1, r, sh, routed, total;
+};
+
+SandwichWs sandwich_ws(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
+                       const ffnq_ffn* shared, int shared_inter)
+{
+    SandwichWs w{};
+    const size_t rows = align_up((size_t)m * hidden * 2, 256);
+    size_t o = 0;
+    w.h1 = o; o += rows;
+    w.r = o; o += rows;
+    w.sh = o; o += align_up(dense_ws(shared->down.fmt, hidden, shared_inter, m, FFNQ_TAIL_RMSNORM, true).total, 256);
+    w.routed = o; o += routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts).total;
+    w.total = m == 0 ? 0 : o;
+    return w;
+}
+
+int moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
+                       const ffnq_ffn* shared, int shared_inter, const uint16_t* shared_norm_w,
+                       const uint16_t* post_norm_w, float eps, const uint16_t* x, const float* logits,
+                       const float* expert_scale, int slot_cap, int32_t* topk_ids, float* topk_w, int32_t* plan,
+                       size_t plan_bytes, uint16_t* resid, void* ws, size_t* ws_bytes, hipStream_t stream)
+{
+    if (!ws_bytes) return FFNQ_ERR_INVALID;
+    if (m < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts) return FFNQ_ERR_INVALID;
+    int rc = check_ffn(experts, hidden, moe_inter);
+    if (rc != FFNQ_OK) return rc;
+    if (!is_int4(experts->gate.fmt) || !is_int4(experts->up.fmt) || !is_int4(experts->down.fmt))
+        return FFNQ_ERR_UNSUPPORTED;
+    if (!shared) return FFNQ_ERR_INVALID;
+    rc = check_ffn(shared, hidden, shared_inter);
+    if (rc != FFNQ_OK) return rc;
+    if (act != FFNQ_ACT_SILU && act != FFNQ_ACT_GELU_TANH) return FFNQ_ERR_UNSUPPORTED;
+    if (!x || !resid || !shared_norm_w || !post_norm_w) return FFNQ_ERR_INVALID;
+    if (misaligned(x) || misaligned(resid) || misaligned(shared_norm_w) || misaligned(post_norm_w))
+        return FFNQ_ERR_INVALID;
+    if (!(eps >= 0.0f && std::isfinite(eps))) return FFNQ_ERR_INVALID;
+    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
+    const size_t rows_bytes = (size_t)m * hidden * 2;
+    if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
+    rc = check_route(logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan, plan_bytes);
+    if (rc != FFNQ_OK) return rc;
+    const SandwichWs L = sandwich_ws(experts, n_experts, hidden, moe_inter, m, top_k, shared, shared_inter);
+    if (!ws) {
+        *ws_bytes = L.total;
+        return FFNQ_OK;
+    }
+    if (*ws_bytes < L.total) return FFNQ_ERR_WORKSPACE;
+    if (misaligned(ws)) return FFNQ_ERR_INVALID;
+    if (m == 0) return FFNQ_OK;
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    uint16_t* h1 = reinterpret_cast<uint16_t*>(base + L.h1);
+    uint16_t* r = reinterpret_cast<uint16_t*>(base + L.r);
+
+    const RouteIn rin_v{logits, expert_scale, slot_cap};
+    const RouteIn* rin = &rin_v;
+    if (!route_in_gu(experts, n_experts, hidden, moe_inter, m, top_k)) {
+        rc = launch_route(logits, expert_scale, m, n_experts, top_k, slot_cap, topk_ids, topk_w, plan, stream);
+        if (rc != FFNQ_OK) return rc;
+        rin = nullptr;
+    }
+    rc = run_dense(true, shared, hidden, shared_inter, m, act, FFNQ_TAIL_RMSNORM, x, h1, shared_norm_w, eps,
+                   base + L.sh, stream);
+    if (rc != FFNQ_OK) return rc;
+    const size_t nrow = (size_t)m * hidden;
+    hipLaunchKernelGGL(zero_u16_kernel, dim3((unsigned)std::min<size_t>((nrow + 255) / 256, 1024)), dim3(256), 0,
+                       stream, r, nrow);
+    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    rc = run_routed(experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan, nullptr, r,
+                    base + L.routed, stream, nullptr, rin);
+    if (rc != FFNQ_OK) return rc;
+    hipLaunchKernelGGL(sandwich_tail_kernel, dim3(m), dim3(kTailThreads), 0, stream, h1, r, post_norm_w, hidden, eps,
+                       resid);
+    return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
 // The allocation-free dense call (ffnq_dense_noalloc) keeps its workspace in
 // this file-scope device array: every GPU the library runs on holds one copy,
 // for the life of the process.  Host code never passes the array's name to a
@@ -1443,6 +1526,18 @@ int ffnq_moe_layer_logits(const ffnq_ffn* experts, int n_experts, int hidden, in
     const RouteIn rin{logits, expert_scale, slot_cap};
     return moe_layer_common(experts, n_experts, hidden, moe_inter, m, top_k, act, shared, shared_inter, shared_gate,
                             x, topk_ids, topk_w, plan, plan_bytes, resid, ws, ws_bytes, stream, &rin);
+}
+
+int ffnq_moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k,
+                            int act, const ffnq_ffn* shared, int shared_inter, const uint16_t* shared_norm_w,
+                            const uint16_t* post_norm_w, float eps, const uint16_t* x, const float* logits,
+                            const float* expert_scale, int slot_cap, int32_t* topk_ids, float* topk_w,
+                            int32_t* plan, size_t plan_bytes, uint16_t* resid, void* ws, size_t* ws_bytes,
+                            hipStream_t stream)
+{
+    return moe_layer_sandwich(experts, n_experts, hidden, moe_inter, m, top_k, act, shared, shared_inter,
+                              shared_norm_w, post_norm_w, eps, x, logits, expert_scale, slot_cap, topk_ids, topk_w,
+                              plan, plan_bytes, resid, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

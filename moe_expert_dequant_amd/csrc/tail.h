@@ -205,4 +205,48 @@ __global__ void __launch_bounds__(256) moe_reduce_kernel(const float* __restrict
     }
 }
 
+// Zero fill of n bf16 values (a kernel rather than a memset node, so that a
+// caller may capture the call in a graph).
+__global__ void __launch_bounds__(256) zero_u16_kernel(uint16_t* __restrict__ p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// The Gemma-style sandwich tail ([qwen/moe_batch.rs] module doc, first
+// bullet: the routed sum starts from zero and the shared branch, normed by
+// its own post-FFN RMSNorm, joins in the layer's sandwich tail).  Per token t
+// (one workgroup): z = h1 + r (the bf16 shared row and the bf16 routed row,
+// added in double, exactly), n = bf16(z / sqrt(mean(z^2) + eps) * w) with the
+// sum of squares, the scale and the product in double, and one raw residual
+// add resid = bf16(resid + n).
+constexpr int kTailThreads = 256;
+
+__global__ void __launch_bounds__(kTailThreads) sandwich_tail_kernel(const uint16_t* __restrict__ h1,
+                                                                     const uint16_t* __restrict__ r,
+                                                                     const uint16_t* __restrict__ w, int n, float eps,
+                                                                     uint16_t* __restrict__ resid)
+{
+    __shared__ double partial[kTailThreads / 64];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* ht = h1 + (size_t)t * n;
+    const uint16_t* rt = r + (size_t)t * n;
+    double ss = 0.0;
+    for (int i = tid; i < n; i += kTailThreads) {
+        const double z = (double)bf16_f32(ht[i]) + (double)bf16_f32(rt[i]);
+        ss += z * z;
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) partial[tid >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int i = 0; i < kTailThreads / 64; ++i) tot += partial[i];
+    const double inv = 1.0 / sqrt(tot / (double)n + (double)eps);
+    uint16_t* o = resid + (size_t)t * n;
+    for (int i = tid; i < n; i += kTailThreads) {
+        const double z = (double)bf16_f32(ht[i]) + (double)bf16_f32(rt[i]);
+        const uint16_t nb = bf16_from_f64(z * inv * (double)bf16_f32(w[i]));
+        o[i] = bf16_from_f64((double)bf16_f32(o[i]) + (double)bf16_f32(nb));
+    }
+}
+
 }  // namespace ffnq

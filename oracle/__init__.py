@@ -22,6 +22,7 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY = 0, -1, -2, -3
+TAIL_NONE, TAIL_RESIDUAL, TAIL_RMSNORM, TAIL_SIGMOID_GATE = 0, 1, 2, 3   # oracle.h OR_TAIL_*
 
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -77,6 +78,7 @@ def _load(path: str):
         "or_moe_route": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp]),
         "or_seeded_sum": (f32, [f32, vp, vp, i32]),
         "or_moe_routed": (i32, [P, P, P, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "or_sandwich_tail": (None, [vp, vp, vp, i32, i32, f32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -286,6 +288,35 @@ def moe_routed(experts: dict, n_experts: int, hidden: int, moe_inter: int, act_k
     if rc != OK:
         raise ValueError(f"oracle moe_routed: status {rc}")
     return out
+
+
+def sandwich_tail(h1: np.ndarray, r: np.ndarray, w: np.ndarray, eps: float, resid: np.ndarray) -> np.ndarray:
+    """The Gemma-style sandwich tail (or_sandwich_tail): resid + bf16(RMSNorm(h1 + r) * w), rounded to bf16."""
+    h1 = _c(h1, np.uint16)
+    r = _c(r, np.uint16)
+    w = _c(w, np.uint16)
+    m, n = h1.shape
+    assert r.shape == (m, n) and w.shape == (n,)
+    out = np.array(resid, dtype=np.uint16, copy=True)
+    lib().or_sandwich_tail(_p(h1), _p(r), _p(w), m, n, eps, _p(out))
+    return out
+
+
+def moe_sandwich_layer(experts: dict, n_experts: int, hidden: int, moe_inter: int, act_kind: int, shared: dict,
+                       shared_inter: int, shared_norm_w: np.ndarray, post_norm_w: np.ndarray, eps: float,
+                       x: np.ndarray, logits: np.ndarray, scale: np.ndarray | None, k: int, cap: int,
+                       resid: np.ndarray):
+    """The Gemma-style routed layer ([qwen/moe_batch.rs] module doc, first bullet), step by step: router
+    top-k with the per-expert scale and the plan; the shared branch with its own RMSNorm tail (h1, bf16);
+    the routed half unseeded, its sum rounded to a bf16 row r (the routed call on a zero row); the
+    sandwich tail.  Returns (status, ids, weights, plan, h1, r, resid_out)."""
+    rc, ids, w, plan = moe_route(logits, k, cap, scale)
+    if rc != OK:
+        return rc, ids, w, plan, None, None, None
+    h1 = shared_expert(shared, hidden, shared_inter, act_kind, TAIL_RMSNORM, x, shared_norm_w, eps)
+    m = h1.shape[0]
+    r = moe_routed(experts, n_experts, hidden, moe_inter, act_kind, x, ids, w, None, np.zeros((m, hidden), np.uint16))
+    return rc, ids, w, plan, h1, r, sandwich_tail(h1, r, post_norm_w, eps, resid)
 
 
 def plan_fields(plan: np.ndarray, m: int, k: int) -> dict:

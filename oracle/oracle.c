@@ -12,7 +12,9 @@
  *                              RMSNorm tail (RMS_EPS = 1e-6, bf16 weight)
  *   [qwen/moe_batch.rs]        module doc and `encode_qwen_layer_moe_batched`: router top-k with
  *                              renormalised weights, union-bounded sub-batches, pair order, phase 1,
- *                              phase 2 seeded with the sigmoid-gated shared expert, raw residual add
+ *                              phase 2 seeded with the sigmoid-gated shared expert, raw residual add;
+ *                              module doc, first bullet: the Gemma-style variant (routed sum from
+ *                              zero, the normed shared branch joining in a sandwich tail)
  *
  * Precision: the pages fix none beyond 2-byte activation buffers, an fp32
  * router and an fp32 phase-2 accumulator.  The oracle therefore works in
@@ -422,4 +424,37 @@ int or_moe_routed(const or_qmat* gate, const or_qmat* up, const or_qmat* down, i
     }
     free(d); free(wt); free(valid);
     return OR_OK;
+}
+
+/* ---- O9: the Gemma-style sandwich tail -----------------------------------------------------
+ * [qwen/moe_batch.rs] module doc, first bullet: Gemma's routed sum starts from
+ * zero (no seed) and its shared branch joins in the layer's sandwich tail after
+ * its own norm ([gemma4/shared_expert.rs] `encode_shared_expert_branch`: the
+ * down projection, then `post_feedforward_layernorm_1` in place, into the bf16
+ * row h1).  The pages print no more of that tail.  Reading taken here: the
+ * join is z = h1 + r, the bf16 shared row plus the bf16 routed row (the
+ * unseeded routed sum rounded once), added exactly; one more RMSNorm with its
+ * own bf16 weight w over z, written as a bf16 row (as every norm on the pages
+ * writes one); then one raw residual add into the stream.  Per token t:
+ *   n = bf16(z / sqrt(mean(z^2) + eps) * w),  resid <- bf16(resid + n). */
+void or_sandwich_tail(const uint16_t* h1, const uint16_t* r, const uint16_t* w, int m, int n, float eps,
+                      uint16_t* resid)
+{
+    double* z = (double*)malloc(sizeof(double) * (size_t)n);
+    for (int t = 0; t < m; ++t) {
+        const uint16_t* ht = h1 + (size_t)t * n;
+        const uint16_t* rt = r + (size_t)t * n;
+        uint16_t* o = resid + (size_t)t * n;
+        double ss = 0.0;
+        for (int i = 0; i < n; ++i) {
+            z[i] = or_bf16_value(ht[i]) + or_bf16_value(rt[i]);
+            ss += z[i] * z[i];
+        }
+        double inv = 1.0 / sqrt(ss / (double)n + (double)eps);
+        for (int i = 0; i < n; ++i) {
+            uint16_t nb = or_bf16_round(z[i] * inv * or_bf16_value(w[i]));
+            o[i] = or_bf16_round(or_bf16_value(o[i]) + or_bf16_value(nb));
+        }
+    }
+    free(z);
 }

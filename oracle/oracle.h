@@ -57,4 +57,6 @@ float or_seeded_sum(float seed, const float* w, const float* d, int k);
 int or_moe_routed(const or_qmat* gate, const or_qmat* up, const or_qmat* down, int n_experts, int hidden,
                   int moe_inter, int m, int k, int act, const uint16_t* x, const int32_t* ids,
                   const float* w, const uint16_t* seed, uint16_t* resid);
+void or_sandwich_tail(const uint16_t* h1, const uint16_t* r, const uint16_t* w, int m, int n, float eps,
+                      uint16_t* resid);
 #endif

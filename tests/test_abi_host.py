@@ -289,3 +289,37 @@ def test_layer_logits_refusals_and_query():
     assert call_layer_logits(f, sh, plan_bytes=4 * fq.plan_ints(3, 2) - 4)[0] == -4
     assert call_layer_logits(ffn(I8, I4, 256, 256), sh)[0] == -2
     assert call_layer_logits(f, sh, ws=addr(60), ws_bytes=n - 256)[0] == -4
+
+
+def call_sandwich(f, sh, E=8, hidden=256, inter=256, sh_inter=512, m=3, k=2, cap=8, plan_bytes=None,
+                  logits=addr(46), norm1=addr(47), norm2=addr(48), eps=1e-6, x=addr(40), ws=None, ws_bytes=0):
+    L = fq.lib()
+    size = C.c_size_t(ws_bytes)
+    pb = 4 * fq.plan_ints(m, k) if plan_bytes is None else plan_bytes
+    rc = L.ffnq_moe_layer_sandwich(C.byref(f), E, hidden, inter, m, k, fq.ACT_GELU_TANH,
+                                   None if sh is None else C.byref(sh), sh_inter, norm1, norm2, eps, x, logits,
+                                   addr(49), cap, addr(41), addr(42), addr(43), pb, addr(50), ws, C.byref(size), None)
+    return rc, size.value
+
+
+def test_layer_sandwich_refusals_and_query():
+    f, sh = ffn(I4, I4, 256, 256), ffn(I8, I8, 256, 512)
+    rc, n = call_sandwich(f, sh)
+    assert rc == 0 and n > 0
+    # workspace: the two bf16 rows, the shared expert's (RMSNorm tail) and the routed half's
+    assert n >= 2 * 3 * 256 * 2 + call_dense(sh, 256, 512, 3, tail=fq.TAIL_RMSNORM, shared=True)[1]
+    assert call_sandwich(f, sh, m=0) == (0, 0)
+    assert call_sandwich(f, None)[0] == -1                      # the shared branch is required
+    assert call_sandwich(f, sh, norm1=None)[0] == -1
+    assert call_sandwich(f, sh, norm2=None)[0] == -1
+    assert call_sandwich(f, sh, norm2=addr(48) + 2)[0] == -1    # misaligned
+    assert call_sandwich(f, sh, eps=float("nan"))[0] == -1
+    assert call_sandwich(f, sh, eps=-1.0)[0] == -1
+    assert call_sandwich(f, sh, logits=None)[0] == -1
+    assert call_sandwich(f, sh, x=addr(50))[0] == -1            # x overlaps resid
+    assert call_sandwich(f, sh, cap=33)[0] == -2
+    assert call_sandwich(f, sh, k=4, cap=3)[0] == -3
+    assert call_sandwich(f, sh, plan_bytes=4 * fq.plan_ints(3, 2) - 4)[0] == -4
+    assert call_sandwich(ffn(I8, I8, 256, 256), sh)[0] == -2    # INT4 experts only
+    assert call_sandwich(f, ffn(I8, I8, 256, 384), sh_inter=512)[0] == -1   # shared shape mismatch
+    assert call_sandwich(f, sh, ws=addr(60), ws_bytes=n - 256)[0] == -4

@@ -170,3 +170,47 @@ def test_graph_replay_moe_layer_logits(tiled):
     want_o = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids_o, w_o, seed_o,
                                inp["resid"])
     check(host16(r), want_o, f"graph moe layer logits replay vs oracle tiled {tiled}")
+
+
+@LAYOUTS
+def test_graph_replay_moe_layer_sandwich(tiled):
+    # the Gemma-style layer (route, shared branch, zero fill, routed half, sandwich
+    # tail) captured once and replayed; replays equal the eager call and the oracle
+    hidden, inter, E, m, k, cap, sh_inter, eps = 512, 256, 16, 3, 4, 8, 384, 1e-6
+    say("graph moe layer sandwich", tiled)
+    inp = gen.sandwich_inputs(hidden, E, inter, m, seed=4747, shared_inter=sh_inter)
+    ex_d = mats_dev(inp["experts"], tiled, E)
+    ex = fq.ffn_struct(ex_d)
+    sh_d, sh = ffn_dev(inp["shared"], tiled)
+    x, r0, lg = dev16(inp["x"]), dev16(inp["resid"]), dev(inp["logits"].astype(np.float32))
+    n1, n2, sc = dev16(inp["shared_norm_w"]), dev16(inp["post_norm_w"]), dev(inp["expert_scale"])
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    ws = fq.Workspace()
+
+    def layer(resid):
+        fq.moe_layer_sandwich(ex, E, hidden, inter, m, k, gen.ACT_GELU_TANH, sh, sh_inter, n1, n2, eps, x, lg, cap,
+                              ids, w, plan, resid, expert_scale=sc, ws=ws)
+
+    want = r0.clone()
+    layer(want)
+    torch.cuda.synchronize()
+    r = r0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(r)
+    for rep in range(4):
+        r.copy_(r0)
+        ids.fill_(-7)
+        plan.fill_(-7)
+        ws.buf.fill_(0x7F)                  # eager work over the workspace the replay must rewrite (h1, r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r, want), rep
+    rc, ids_o, w_o, plan_o, h1_o, r_o, want_o = oracle.moe_sandwich_layer(
+        inp["experts"], E, hidden, inter, gen.ACT_GELU_TANH, inp["shared"], sh_inter, inp["shared_norm_w"],
+        inp["post_norm_w"], eps, inp["x"], inp["logits"], inp["expert_scale"], k, cap, inp["resid"])
+    assert rc == 0 and np.array_equal(ids.cpu().numpy(), ids_o) and np.array_equal(plan.cpu().numpy(), plan_o)
+    check(host16(r), want_o, f"graph moe layer sandwich replay vs oracle tiled {tiled}")

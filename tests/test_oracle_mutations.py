@@ -72,6 +72,21 @@ MUTATIONS = [
      [("r.s = (const uint16_t*)w->s + (size_t)e * n * (k / 64);",
        "r.s = (const uint16_t*)w->s + (size_t)e * n * (k / 128);")],
      [P.test_moe_labelled_experts_seeded]),
+    ("sandwich join drops the routed row",
+     [("z[i] = or_bf16_value(ht[i]) + or_bf16_value(rt[i]);", "z[i] = or_bf16_value(ht[i]);")],
+     [P.test_sandwich_tail_hand, P.test_sandwich_tail_invariants,
+      lambda: P.test_sandwich_layer_identical_experts("ones")]),
+    ("sandwich tail norm weight dropped",
+     [("uint16_t nb = or_bf16_round(z[i] * inv * or_bf16_value(w[i]));", "uint16_t nb = or_bf16_round(z[i] * inv);")],
+     [P.test_sandwich_tail_hand]),
+    ("sandwich norm row added before its bf16 rounding",
+     [("o[i] = or_bf16_round(or_bf16_value(o[i]) + or_bf16_value(nb));",
+       "o[i] = or_bf16_round(or_bf16_value(o[i]) + z[i] * inv * or_bf16_value(w[i])); (void)nb;")],
+     [P.test_sandwich_tail_hand]),
+    ("sandwich eps outside the square root",
+     [("double inv = 1.0 / sqrt(ss / (double)n + (double)eps);",
+       "double inv = 1.0 / (sqrt(ss / (double)n) + (double)eps);")],
+     [P.test_sandwich_tail_hand]),
 ]
 
 

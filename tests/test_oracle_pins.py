@@ -697,3 +697,81 @@ def test_moe_labelled_experts_seeded():
     assert diff.mean() < 0.01   # act's fp32 rounding may differ from torch's in the last ulp
     assert np.all(np.abs(gen.bf16_to_f32(got[diff]).astype(np.float64) - gen.bf16_to_f32(want[diff])) <=
                   np.abs(gen.bf16_to_f32(want[diff])) * 2 ** -7 + 1e-30)
+
+
+# ---------------------------------------------------------------------------
+# O9: the Gemma-style sandwich tail and the layer it ends
+
+
+def _bits(rows):
+    return gen.bf16_bits(np.array(rows, dtype=np.float64))
+
+
+def test_sandwich_tail_hand():
+    for case in golden("sandwich_hand.json")["cases"]:
+        out = oracle.sandwich_tail(_bits(case["h1"]), _bits(case["r"]), _bits(case["w"]), case["eps"],
+                                   _bits(case["resid"]))
+        assert out.tolist() == case["expect_bits"], case["name"]
+
+
+def test_sandwich_tail_invariants():
+    rng = np.random.default_rng(81)
+    m, n = 3, 96
+    h1 = gen.bf16_bits(rng.standard_normal((m, n)))
+    r = gen.bf16_bits(rng.standard_normal((m, n)))
+    w = gen.norm_weight(82, n)
+    resid = gen.act_rows(83, m, n)
+    a = oracle.sandwich_tail(h1, r, w, 0.0, resid)
+    # the join is a sum: the two rows commute
+    assert np.array_equal(a, oracle.sandwich_tail(r, h1, w, 0.0, resid))
+    # with eps = 0 the norm ignores a power-of-two scale of the joined row (bf16 doubling is exact)
+    h2 = gen.bf16_bits(2.0 * gen.bf16_to_f32(h1).astype(np.float64))
+    r2 = gen.bf16_bits(2.0 * gen.bf16_to_f32(r).astype(np.float64))
+    assert np.array_equal(a, oracle.sandwich_tail(h2, r2, w, 0.0, resid))
+    # an all-zero join adds +0 (eps > 0): the stream is unchanged
+    z = np.zeros((m, n), np.uint16)
+    assert np.array_equal(oracle.sandwich_tail(z, z, w, 1e-6, resid), resid)
+    # rows are independent: one token at a time gives the same rows
+    for t in range(m):
+        one = oracle.sandwich_tail(h1[t:t + 1], r[t:t + 1], w, 0.0, resid[t:t + 1])
+        assert np.array_equal(one[0], a[t])
+
+
+@pytest.mark.parametrize("scale_kind", ["ones", "two"])
+def test_sandwich_layer_identical_experts(scale_kind):
+    """Routed experts that are all one FFN F: with route weights summing to 1 the
+    unseeded routed sum is F(x_t) itself (to the fp32 rounding of the weighted
+    sum), and with every expert scale 2 it is 2 F(x_t); so the layer is the
+    sandwich tail of the shared branch's normed row and bf16(c F(x_t)), made
+    here from oracle.shared_expert alone.  A routed sum seeded with the shared
+    row, or a join that drops either row, fails this."""
+    hidden, inter, sh_inter, E, k, m = 128, 128, 192, 6, 3, 4
+    one = gen.ffn(gen.FMT_INT4_AFFINE_G64, gen.FMT_INT4_AFFINE_G64, hidden, inter, 71)
+    stack = {n: dict(one[n], q=np.stack([one[n]["q"]] * E), s=np.stack([one[n]["s"]] * E),
+                     z=np.stack([one[n]["z"]] * E)) for n in one}
+    shared = gen.ffn(gen.FMT_INT8_ROW, gen.FMT_INT8_ROW, hidden, sh_inter, 72, row_scales=True)
+    x = gen.act_rows(73, m, hidden)
+    resid = gen.act_rows(74, m, hidden)
+    lg = gen.router_logits(75, m, E)
+    w1, wp = gen.norm_weight(76, hidden), gen.norm_weight(77, hidden)
+    c = 1.0 if scale_kind == "ones" else 2.0
+    scale = None if scale_kind == "ones" else np.full(E, c, np.float32)
+    act, eps = gen.ACT_GELU_TANH, 1e-6
+    rc, ids, w, plan, h1, r, out = oracle.moe_sandwich_layer(stack, E, hidden, inter, act, shared, sh_inter, w1, wp,
+                                                             eps, x, lg, scale, k, 8, resid)
+    assert rc == 0
+    f = oracle.shared_expert(one, hidden, inter, act, gen.TAIL_NONE, x, None)       # bf16(F(x_t))
+    rc_closed = gen.bf16_bits(c * gen.bf16_to_f32(f).astype(np.float64))             # exact: c is 1 or 2
+    d = np.abs(gen.bf16_to_f32(r).astype(np.float64) - gen.bf16_to_f32(rc_closed))
+    assert np.all(d <= np.abs(gen.bf16_to_f32(rc_closed)) * 2 ** -7 + 1e-30)
+    assert np.mean(r != rc_closed) < 0.05
+    h1_closed = oracle.shared_expert(shared, hidden, sh_inter, act, gen.TAIL_RMSNORM, x, w1, eps)
+    assert np.array_equal(h1, h1_closed)
+    want = oracle.sandwich_tail(h1_closed, rc_closed, wp, eps, resid)
+    g = gen.bf16_to_f32(out).astype(np.float64)
+    wv = gen.bf16_to_f32(want).astype(np.float64)
+    assert np.all(np.abs(g - wv) <= np.abs(wv) * 2 ** -6 + 2 ** -10)
+    assert np.mean(out != want) < 0.1
+    # the shared row alone (routed term dropped) is far from the layer
+    alone = oracle.sandwich_tail(h1_closed, np.zeros_like(h1_closed), wp, eps, resid)
+    assert np.mean(alone != out) > 0.5
