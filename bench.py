@@ -418,6 +418,57 @@ def time_router_gemv(x, m: int, hidden: int, E: int, calls: int = 50) -> float:
     return st.elapsed_time(en) * 1e3 / calls
 
 
+def run_streamed(c: int, m: int, steps: int, warmup: int) -> dict:
+    """Workload c's routed half with its experts in pinned host memory (ffnq_moe_routed_streamed, slot cache of
+    `cap` slots): `cold` empties the slot table before every call, so every union expert crosses PCIe (the
+    expert-store case of a model larger than HBM); `warm` keeps it, so repeated routes copy nothing.  Each call
+    reads the routes back to the host once, so the time is the wall clock of the call through a synchronize."""
+    import torch
+    import gen
+    import moe_expert_dequant_amd as fq
+
+    cfg = gen.CONFIGS[c]
+    inp = gen.config_inputs(c, m)
+    hidden, E, inter, k, cap = cfg["hidden"], cfg["n_experts"], cfg["moe_inter"], cfg["top_k"], cfg["cap"]
+    d = {n: fq.pack(fq.to_device(inp["experts"][n]), E) for n in ("gate", "up", "down")}
+    hx_d, hx = fq.host_experts(d)
+    del d
+    logits = torch.from_numpy(np.ascontiguousarray(inp["logits"], dtype=np.float32)).cuda()
+    ids = torch.zeros((m, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.zeros((fq.plan_ints(m, k),), dtype=torch.int32, device="cuda")
+    fq.moe_route(logits, m, E, k, cap, ids, w, plan)
+    x, resid = _dev16(inp["x"]), _dev16(inp["resid"])
+    cache = fq.SlotCache(cap, hidden, inter)
+    ws = fq.Workspace()
+    torch.cuda.synchronize()
+    union = len(set(ids.cpu().numpy().ravel().tolist()))
+    ebytes = 2 * weight_bytes(cfg["fmt"], inter, hidden) + weight_bytes(cfg["fmt"], hidden, inter)
+
+    def timed(cold: bool, n: int):
+        t = []
+        for _ in range(n):
+            if cold:
+                cache.expert[:] = -1
+            t0 = time.perf_counter()
+            fq.moe_routed_streamed(hx, E, hidden, inter, m, k, cfg["act"], x, ids, w, plan, None, resid, cache, ws=ws)
+            torch.cuda.synchronize()
+            t.append(time.perf_counter() - t0)
+        return float(np.median(t))
+
+    timed(True, warmup)
+    copied0 = cache.copied
+    cold = timed(True, steps)
+    cold_copies = (cache.copied - copied0) / steps
+    timed(False, 2)
+    copied0 = cache.copied
+    warm = timed(False, steps)
+    return dict(union=union, expert_bytes=ebytes, slots=cap, cold_call_us=cold * 1e6, cold_tokens_per_s=m / cold,
+                cold_experts_copied_per_call=cold_copies, pcie_GBs=union * ebytes / cold / 1e9,
+                warm_call_us=warm * 1e6, warm_tokens_per_s=m / warm,
+                warm_experts_copied_per_call=(cache.copied - copied0) / steps)
+
+
 def run_configs(steps: int, warmup: int) -> dict:
     import gen
     out = {}
@@ -425,6 +476,9 @@ def run_configs(steps: int, warmup: int) -> dict:
         cfg = gen.CONFIGS[c]
         out[cfg["name"]] = {f"M={m}": run_config(c, m, steps, warmup) for m in cfg["ms"]}
         print(f"# config {c} done", file=sys.stderr, flush=True)
+    # the Qwen-shaped routed half streamed from host memory through the slot cache
+    out["qwen3-moe-int4-streamed-from-host"] = {f"M={m}": run_streamed(3, m, 30, 3) for m in (1, 4)}
+    print("# streamed done", file=sys.stderr, flush=True)
     return out
 
 
@@ -542,6 +596,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--rowmajor", action="store_true", help="stream the row-major weights instead of the tiled ones")
     ap.add_argument("--no-configs", action="store_true", help="skip the steady-state timing of every workload shape")
+    ap.add_argument("--streamed", action="store_true",
+                    help="time only the Qwen-shaped routed half streamed from host memory at --m tokens")
     ap.add_argument("--config", type=int, default=None,
                     help="time only workload shape CONFIG at --m tokens (steady state; for kernel traces)")
     args = ap.parse_args()
@@ -556,6 +612,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.streamed:
+        print(json.dumps({"config": 3, "m": args.m, "streamed": run_streamed(3, args.m, args.steps, args.warmup)}),
+              flush=True)
         return
     if args.config is not None:
         r = run_config(args.config, args.m, args.steps, args.warmup)
@@ -628,7 +688,7 @@ def main():
     if not (args.no_configs or args.single):
         out["configs"] = run_configs(100, 10)
         # every workload shape's gate/up and down kernels against their roofline
-        out["roofline_kernels"] = [k for cf in out["configs"].values() for r in cf.values() for k in r["kernels"]]
+        out["roofline_kernels"] = [k for cf in out["configs"].values() for r in cf.values() for k in r.get("kernels", [])]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

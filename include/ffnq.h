@@ -154,6 +154,23 @@ typedef struct ffnq_ffn {
     ffnq_qmat gate, up, down;
 } ffnq_ffn;
 
+/* A device slot cache for routed experts streamed from host memory
+ * ([qwen/moe_batch.rs] `encode_qwen_layer_moe_batched`: each sub-batch's
+ * expert union is read into the expert cache's slots before its routed phases
+ * run; the module doc: a sub-batch's union never exceeds the slot count).
+ * The caller owns every field and keeps them between calls, so experts that
+ * stay in their slots are not copied again. */
+typedef struct ffnq_slot_cache {
+    void* slots;          /* device: n_slots tiled gate matrices, then n_slots up, then n_slots down
+                             (each at its ffnq_packed_bytes stride, as a stacked tiled expert tensor) */
+    size_t slots_bytes;   /* bytes at slots: >= n_slots * (2 * packed(gate) + packed(down)) */
+    int32_t n_slots;      /* 1 <= n_slots <= FFNQ_MAX_EXPERTS */
+    int32_t* expert;      /* host [n_slots]: the expert each slot holds, -1 if none (in/out) */
+    uint64_t* last_use;   /* host [n_slots]: the use stamp of each slot (in/out) */
+    uint64_t clock;       /* the last stamp handed out (in/out) */
+    uint64_t copied;      /* experts copied into slots, counted over calls (in/out) */
+} ffnq_slot_cache;
+
 /* ---- ffnq_dense ------------------------------------------------------------
  * Dense FFN half of a layer, for m token-major rows ([llama/dense.rs], the
  * module-doc equation and `encode_llama_layer_dense`):
@@ -385,6 +402,43 @@ FFNQ_API int ffnq_moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int
                                      int slot_cap, int32_t* topk_ids, float* topk_w, int32_t* plan,
                                      size_t plan_bytes, uint16_t* resid, void* ws, size_t* ws_bytes,
                                      hipStream_t stream);
+
+/* ---- ffnq_moe_routed_streamed ----------------------------------------------
+ * ffnq_moe_routed_batched for experts that live in host memory
+ * ([qwen/moe_batch.rs] `encode_qwen_layer_moe_batched` with
+ * `plan_and_stream_union`: the host plans each sub-batch from the routes, the
+ * sub-batch's union experts are read into the cache slots after the previous
+ * sub-batch is done, then its phase 1 and phase 2 run on those slots).  Per
+ * sub-batch of the plan, in order, on `stream`: every union expert that no
+ * slot holds is copied (host to device) into a slot that holds no expert of
+ * this union -- an empty one first, else the least recently used; then the
+ * routed phases run on the sub-batch's tokens with the slots as the experts.
+ * The result is that of ffnq_moe_routed_batched on the same experts resident
+ * (each token's arithmetic is the same; kernel shapes follow the sub-batch's
+ * size, so the fp32 summation order may differ).
+ * host_experts: tiled INT4 experts (FFNQ_FMT_INT4_AFFINE_G64_TILED, packed by
+ *               ffnq_pack and copied out) whose q pointers address host
+ *               memory, pinned (hipHostMalloc) for the copies to be
+ *               asynchronous.  UNSUPPORTED for any other format.
+ * x, topk_ids, topk_w, plan, seed, resid: as for ffnq_moe_routed_batched.
+ * cache:        the slot cache; FFNQ_ERR_CAPACITY if a sub-batch's union has more
+ *               experts than it has slots (the pages refuse rather than
+ *               loop: plan with slot_cap <= n_slots).
+ * host_staging: host int32 [FFNQ_PLAN_INTS(m, top_k) + m * top_k], pinned:
+ *               the call copies the plan and the ids there and waits for the
+ *               stream (the host's read-back of the routes), then checks
+ *               them: a plan that is not one ffnq_moe_route could write for
+ *               these ids (bounds, sub-batch ranges, union entries, pair
+ *               lists) is refused with FFNQ_ERR_INVALID before any copy.
+ * The call synchronises `stream` once (the read-back) and so cannot be
+ * captured in a graph.  Workspace: the routed half's at m tokens and n_slots
+ * experts, plus one sub-batch's ids and plan; ws == NULL returns the size.
+ */
+FFNQ_API int ffnq_moe_routed_streamed(const ffnq_ffn* host_experts, int n_experts, int hidden, int moe_inter,
+                                      int m, int top_k, int act, const uint16_t* x, const int32_t* topk_ids,
+                                      const float* topk_w, const int32_t* plan, const uint16_t* seed,
+                                      uint16_t* resid, ffnq_slot_cache* cache, int32_t* host_staging,
+                                      void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /* ---- ffnq_packed_bytes / ffnq_pack -----------------------------------------
  * Bytes of one n x k matrix (one expert) in a tiled format; fmt may name the

@@ -31,7 +31,7 @@ OK = 0
 STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSPACE", -5: "HIP"}
 EXPORTS = ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
            "ffnq_moe_routed_batched",
-           "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich",
+           "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich", "ffnq_moe_routed_streamed",
            "ffnq_status_string", "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
 
 
@@ -53,6 +53,11 @@ class QMat(C.Structure):
 
 class Ffn(C.Structure):
     _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class SlotCacheC(C.Structure):
+    _fields_ = [("slots", C.c_void_p), ("slots_bytes", C.c_size_t), ("n_slots", C.c_int32),
+                ("expert", C.c_void_p), ("last_use", C.c_void_p), ("clock", C.c_uint64), ("copied", C.c_uint64)]
 
 
 _lib = None
@@ -78,9 +83,11 @@ def lib():
                                             C.c_size_t, vp, vp, sz, vp]
         L.ffnq_moe_layer_sandwich.argtypes = [FP, i32, i32, i32, i32, i32, i32, FP, i32, vp, vp, f32, vp, vp, vp,
                                               i32, vp, vp, vp, C.c_size_t, vp, vp, sz, vp]
+        L.ffnq_moe_routed_streamed.argtypes = [FP, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                               C.POINTER(SlotCacheC), vp, vp, sz, vp]
         for f in ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
                   "ffnq_moe_routed_batched",
-                  "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich"):
+                  "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich", "ffnq_moe_routed_streamed"):
             getattr(L, f).restype = C.c_int
         L.ffnq_status_string.argtypes = [C.c_int]
         L.ffnq_status_string.restype = C.c_char_p
@@ -266,6 +273,44 @@ def moe_layer_sandwich(experts: Ffn, n_experts: int, hidden: int, moe_inter: int
             _ptr(topk_ids), _ptr(topk_w), _ptr(plan), nbytes, _ptr(resid))
     buf, n = _ws(L.ffnq_moe_layer_sandwich, args, ws)
     _check("ffnq_moe_layer_sandwich", L.ffnq_moe_layer_sandwich(*args, _ptr(buf), C.byref(n), _stream(stream)))
+
+
+class SlotCache:
+    """A device slot cache for routed experts streamed from host memory (ffnq_slot_cache): n_slots slots sized
+    for one tiled INT4 expert of (hidden, moe_inter) each, with the host-side slot table kept between calls."""
+
+    def __init__(self, n_slots: int, hidden: int, moe_inter: int, device="cuda"):
+        import numpy as np
+        gb = packed_bytes(FMT_INT4_AFFINE_G64_TILED, moe_inter, hidden)
+        db = packed_bytes(FMT_INT4_AFFINE_G64_TILED, hidden, moe_inter)
+        self.slots = torch.empty(n_slots * (2 * gb + db), dtype=torch.uint8, device=device)
+        self.expert = np.full(n_slots, -1, np.int32)
+        self.last_use = np.zeros(n_slots, np.uint64)
+        self.c = SlotCacheC(self.slots.data_ptr(), self.slots.numel(), n_slots, self.expert.ctypes.data,
+                            self.last_use.ctypes.data, 0, 0)
+
+    @property
+    def copied(self) -> int:
+        return int(self.c.copied)
+
+
+def host_experts(packed: dict) -> tuple:
+    """Pinned host copies of tiled, packed expert tensors (as fq.pack returns them) and their Ffn struct."""
+    h = {n: dict(packed[n], q=packed[n]["q"].cpu().pin_memory()) for n in ("gate", "up", "down")}
+    return h, ffn_struct(h)
+
+
+def moe_routed_streamed(host_ffn: Ffn, n_experts: int, hidden: int, moe_inter: int, m: int, top_k: int, act: int,
+                        x, topk_ids, topk_w, plan, seed, resid, cache: SlotCache, ws: Workspace | None = None,
+                        stream=None):
+    """ffnq_moe_routed_streamed: the routed half with the experts in (pinned) host memory, each sub-batch's
+    union copied into the cache's slots first."""
+    L = lib()
+    staging = torch.empty(plan_ints(m, top_k) + m * top_k, dtype=torch.int32).pin_memory()
+    args = (C.byref(host_ffn), n_experts, hidden, moe_inter, m, top_k, act, _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+            _ptr(plan), _ptr(seed), _ptr(resid), C.byref(cache.c), staging.data_ptr())
+    buf, n = _ws(L.ffnq_moe_routed_streamed, args, ws)
+    _check("ffnq_moe_routed_streamed", L.ffnq_moe_routed_streamed(*args, _ptr(buf), C.byref(n), _stream(stream)))
 
 
 def workspace_bytes(kind: str, *args) -> int:

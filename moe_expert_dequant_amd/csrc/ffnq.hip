@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "ffnq.h"
 #include "device.h"
@@ -1330,6 +1331,193 @@ int moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int hidden, int m
 }
 
 // ---------------------------------------------------------------------------
+// Routed experts streamed from host memory through a slot cache
+// (ffnq_moe_routed_streamed).
+
+// Whether the host copy of a plan and its ids (m tokens, k per token) is one
+// that ffnq_moe_route could write: sub-batch bounds in order and covering the
+// tokens, unions of 1..min(32, n_slots) distinct valid experts, every pair's
+// slot inside its sub-batch's union and naming its id's expert, and the pair
+// lists a permutation of each sub-batch's pairs by slot.  FFNQ_OK,
+// FFNQ_ERR_CAPACITY (a union larger than the cache) or FFNQ_ERR_INVALID.
+int check_host_plan(const int32_t* plan, const int32_t* ids, int m, int k, int n_experts, int n_slots)
+{
+    const int P = m * k;
+    const int32_t* tok = plan + 1;
+    const int32_t* uni = plan + (m + 2);
+    const int32_t* uexp = plan + (2 * m + 3);
+    const int32_t* pslot = plan + (2 * m + 3 + P);
+    const int32_t* spb = plan + (2 * m + 3 + 2 * P);
+    const int32_t* sp = plan + (2 * m + 4 + 3 * P);
+    const int S = plan[0];
+    if (S < 1 || S > m || tok[0] != 0 || uni[0] != 0 || tok[S] != m) return FFNQ_ERR_INVALID;
+    std::vector<char> seen((size_t)P, 0);
+    for (int b = 0; b < S; ++b) {
+        const int t0 = tok[b], t1 = tok[b + 1], u0 = uni[b], u1 = uni[b + 1];
+        if (t1 <= t0 || t1 > m || u1 <= u0 || u1 > P) return FFNQ_ERR_INVALID;
+        if (u1 - u0 > std::min(FFNQ_MAX_SLOTS, n_slots)) return FFNQ_ERR_CAPACITY;
+        for (int j = u0; j < u1; ++j) {
+            if (uexp[j] < 0 || uexp[j] >= n_experts) return FFNQ_ERR_INVALID;
+            for (int j2 = u0; j2 < j; ++j2)
+                if (uexp[j2] == uexp[j]) return FFNQ_ERR_INVALID;
+        }
+        for (int p = t0 * k; p < t1 * k; ++p) {
+            const int j = pslot[p];
+            if (j < 0 || j >= u1 - u0 || uexp[u0 + j] != ids[p]) return FFNQ_ERR_INVALID;
+        }
+        if (spb[u0] < 0 || spb[u1] - spb[u0] != (t1 - t0) * k || spb[u1] > P) return FFNQ_ERR_INVALID;
+        for (int j = u0; j < u1; ++j) {
+            if (spb[j + 1] < spb[j]) return FFNQ_ERR_INVALID;
+            for (int i = spb[j]; i < spb[j + 1]; ++i) {
+                if (sp[i] < t0 * k || sp[i] >= t1 * k || pslot[sp[i]] != j - u0 || seen[sp[i]]) return FFNQ_ERR_INVALID;
+                seen[sp[i]] = 1;
+            }
+        }
+    }
+    if (uni[S] > P) return FFNQ_ERR_INVALID;
+    return FFNQ_OK;
+}
+
+struct StreamWs {
+    size_t ids, plan, routed, total;
+};
+
+StreamWs stream_ws(const ffnq_ffn* experts, int n_slots, int hidden, int moe_inter, int m, int k)
+{
+    StreamWs w{};
+    size_t o = 0;
+    w.ids = o; o += align_up((size_t)m * k * 4, 256);
+    w.plan = o; o += align_up((size_t)FFNQ_PLAN_INTS((size_t)m, (size_t)k) * 4, 256);
+    w.routed = o; o += routed_ws(experts->down.fmt, hidden, moe_inter, m, k, n_slots).total;
+    w.total = m == 0 ? 0 : o;
+    return w;
+}
+
+int moe_routed_streamed(const ffnq_ffn* hx, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
+                        const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
+                        const uint16_t* seed, uint16_t* resid, ffnq_slot_cache* cache, int32_t* host_staging,
+                        void* ws, size_t* ws_bytes, hipStream_t stream)
+{
+    if (!ws_bytes || !cache) return FFNQ_ERR_INVALID;
+    if (m < 0 || n_experts <= 0 || n_experts > FFNQ_MAX_EXPERTS || top_k < 1 || top_k > n_experts)
+        return FFNQ_ERR_INVALID;
+    int rc = check_ffn(hx, hidden, moe_inter);
+    if (rc != FFNQ_OK) return rc;
+    const int tf = FFNQ_FMT_INT4_AFFINE_G64_TILED;
+    if (hx->gate.fmt != tf || hx->up.fmt != tf || hx->down.fmt != tf) return FFNQ_ERR_UNSUPPORTED;
+    if (act != FFNQ_ACT_SILU && act != FFNQ_ACT_GELU_TANH) return FFNQ_ERR_UNSUPPORTED;
+    if (!x || !topk_ids || !topk_w || !plan || !resid || !host_staging) return FFNQ_ERR_INVALID;
+    if (misaligned(x) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(plan) || misaligned(resid) ||
+        (seed && misaligned(seed)))
+        return FFNQ_ERR_INVALID;
+    if ((long long)m * top_k > (1 << 28)) return FFNQ_ERR_INVALID;
+    const size_t rows_bytes = (size_t)m * hidden * 2;
+    if (m > 0 && overlap(x, rows_bytes, resid, rows_bytes)) return FFNQ_ERR_INVALID;
+    const int ns = cache->n_slots;
+    if (ns < 1 || ns > FFNQ_MAX_EXPERTS || !cache->slots || misaligned(cache->slots) || !cache->expert ||
+        !cache->last_use)
+        return FFNQ_ERR_INVALID;
+    const size_t gb = (size_t)tiled_expert_bytes(hx->gate), db = (size_t)tiled_expert_bytes(hx->down);
+    if (cache->slots_bytes < (size_t)ns * (2 * gb + db)) return FFNQ_ERR_INVALID;
+    for (int s = 0; s < ns; ++s)
+        if (cache->expert[s] < -1 || cache->expert[s] >= n_experts) return FFNQ_ERR_INVALID;
+    const StreamWs L = stream_ws(hx, ns, hidden, moe_inter, m, top_k);
+    if (!ws) {
+        *ws_bytes = L.total;
+        return FFNQ_OK;
+    }
+    if (*ws_bytes < L.total) return FFNQ_ERR_WORKSPACE;
+    if (misaligned(ws)) return FFNQ_ERR_INVALID;
+    if (m == 0) return FFNQ_OK;
+
+    // the host's read-back of the routes
+    const int P = m * top_k;
+    const size_t pints = (size_t)FFNQ_PLAN_INTS((size_t)m, (size_t)top_k);
+    int32_t* hplan = host_staging;
+    int32_t* hids = host_staging + pints;
+    if (hipMemcpyAsync(hplan, plan, pints * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(hids, topk_ids, (size_t)P * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return FFNQ_ERR_HIP;
+    rc = check_host_plan(hplan, hids, m, top_k, n_experts, ns);
+    if (rc != FFNQ_OK) return rc;
+
+    // the slots as a stacked tiled expert tensor of ns experts
+    unsigned char* sbase = static_cast<unsigned char*>(cache->slots);
+    ffnq_ffn sx = *hx;
+    sx.gate.q = sbase;
+    sx.up.q = sbase + (size_t)ns * gb;
+    sx.down.q = sbase + (size_t)ns * 2 * gb;
+    const unsigned char* hg = static_cast<const unsigned char*>(hx->gate.q);
+    const unsigned char* hu = static_cast<const unsigned char*>(hx->up.q);
+    const unsigned char* hd = static_cast<const unsigned char*>(hx->down.q);
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    int32_t* sub_ids = reinterpret_cast<int32_t*>(base + L.ids);
+    int32_t* sub_plan = reinterpret_cast<int32_t*>(base + L.plan);
+
+    const int S = hplan[0];
+    const int32_t* tok = hplan + 1;
+    const int32_t* uni = hplan + (m + 2);
+    const int32_t* uexp = hplan + (2 * m + 3);
+    std::vector<char> in_use(ns);
+    for (int b = 0; b < S; ++b) {
+        const int t0 = tok[b], t1 = tok[b + 1], u0 = uni[b], u1 = uni[b + 1], U = u1 - u0;
+        SubPlanParams sp{};
+        sp.plan = plan;
+        sp.m = m;
+        sp.k = top_k;
+        sp.t0 = t0;
+        sp.t1 = t1;
+        sp.u0 = u0;
+        sp.u1 = u1;
+        sp.ids_out = sub_ids;
+        sp.plan_out = sub_plan;
+        std::fill(in_use.begin(), in_use.end(), 0);
+        // hits first, so that no miss evicts an expert this union still needs
+        for (int j = 0; j < U; ++j) {
+            sp.slot_of[j] = -1;
+            for (int s = 0; s < ns; ++s)
+                if (cache->expert[s] == uexp[u0 + j]) {
+                    sp.slot_of[j] = s;
+                    in_use[s] = 1;
+                    break;
+                }
+        }
+        for (int j = 0; j < U; ++j) {
+            if (sp.slot_of[j] >= 0) continue;
+            int v = -1;
+            for (int s = 0; s < ns; ++s) {
+                if (in_use[s]) continue;
+                if (v < 0 || (cache->expert[s] < 0 && cache->expert[v] >= 0) ||
+                    ((cache->expert[s] < 0) == (cache->expert[v] < 0) && cache->last_use[s] < cache->last_use[v]))
+                    v = s;
+            }
+            const size_t e = (size_t)uexp[u0 + j];
+            if (hipMemcpyAsync(sbase + (size_t)v * gb, hg + e * gb, gb, hipMemcpyHostToDevice, stream) != hipSuccess ||
+                hipMemcpyAsync(sbase + (size_t)(ns + v) * gb, hu + e * gb, gb, hipMemcpyHostToDevice, stream) !=
+                    hipSuccess ||
+                hipMemcpyAsync(sbase + (size_t)ns * 2 * gb + (size_t)v * db, hd + e * db, db, hipMemcpyHostToDevice,
+                               stream) != hipSuccess) {
+                cache->expert[v] = -1;   // its contents are unknown now
+                return FFNQ_ERR_HIP;
+            }
+            cache->expert[v] = (int32_t)e;
+            ++cache->copied;
+            sp.slot_of[j] = v;
+            in_use[v] = 1;
+        }
+        for (int j = 0; j < U; ++j) cache->last_use[sp.slot_of[j]] = ++cache->clock;
+        hipLaunchKernelGGL(sub_plan_kernel, dim3(1), dim3(256), 0, stream, sp);
+        if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+        rc = run_routed(&sx, ns, hidden, moe_inter, t1 - t0, top_k, act, x + (size_t)t0 * hidden, sub_ids,
+                        topk_w + (size_t)t0 * top_k, sub_plan, seed ? seed + (size_t)t0 * hidden : nullptr,
+                        resid + (size_t)t0 * hidden, base + L.routed, stream, nullptr);
+        if (rc != FFNQ_OK) return rc;
+    }
+    return FFNQ_OK;
+}
+
+// ---------------------------------------------------------------------------
 // The allocation-free dense call (ffnq_dense_noalloc) keeps its workspace in
 // this file-scope device array: every GPU the library runs on holds one copy,
 // for the life of the process.  Host code never passes the array's name to a
@@ -1538,6 +1726,15 @@ int ffnq_moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int hidden, 
     return moe_layer_sandwich(experts, n_experts, hidden, moe_inter, m, top_k, act, shared, shared_inter,
                               shared_norm_w, post_norm_w, eps, x, logits, expert_scale, slot_cap, topk_ids, topk_w,
                               plan, plan_bytes, resid, ws, ws_bytes, stream);
+}
+
+int ffnq_moe_routed_streamed(const ffnq_ffn* host_experts, int n_experts, int hidden, int moe_inter, int m,
+                             int top_k, int act, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                             const int32_t* plan, const uint16_t* seed, uint16_t* resid, ffnq_slot_cache* cache,
+                             int32_t* host_staging, void* ws, size_t* ws_bytes, hipStream_t stream)
+{
+    return moe_routed_streamed(host_experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan,
+                               seed, resid, cache, host_staging, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -632,4 +632,54 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// One sub-batch of a routing plan as a plan of its own, over the experts held
+// in a slot cache ([qwen/moe_batch.rs] `encode_qwen_layer_moe_batched`: each
+// sub-batch's union is streamed into the expert slots, then its routed phases
+// run on them).  Sub-batch tokens [t0, t1), union entries [u0, u1); union
+// entry j is held by slot slot_of[j].  Writes ids (the slot holding each
+// pair's expert, [m_b][k]) and the plan of m_b = t1 - t0 tokens with one
+// sub-batch: union experts = the slots, pair slots unchanged, the union's pair
+// lists shifted to the sub-batch's own pair numbers; unused entries -1, as
+// ffnq_moe_route leaves them.  One workgroup; the host has checked the plan.
+struct SubPlanParams {
+    const int32_t* plan;   // the whole batch's plan (m tokens, k per token)
+    int m, k;
+    int t0, t1, u0, u1;
+    int32_t slot_of[32];
+    int32_t* ids_out;      // [m_b * k]
+    int32_t* plan_out;     // FFNQ_PLAN_INTS(m_b, k) ints
+};
+
+__global__ void __launch_bounds__(256) sub_plan_kernel(SubPlanParams p)
+{
+    const int tid = threadIdx.x;
+    const int mb = p.t1 - p.t0, Pb = mb * p.k, U = p.u1 - p.u0, P = p.m * p.k;
+    const int32_t* pslot = p.plan + (2 * p.m + 3 + P);
+    const int32_t* spb = p.plan + (2 * p.m + 3 + 2 * P);
+    const int32_t* sp = p.plan + (2 * p.m + 4 + 3 * P);
+    int32_t* o = p.plan_out;
+    int32_t* o_tok = o + 1;
+    int32_t* o_uni = o + (mb + 2);
+    int32_t* o_uexp = o + (2 * mb + 3);
+    int32_t* o_pslot = o + (2 * mb + 3 + Pb);
+    int32_t* o_spb = o + (2 * mb + 3 + 2 * Pb);
+    int32_t* o_sp = o + (2 * mb + 4 + 3 * Pb);
+    const int s0 = spb[p.u0];
+    for (int i = tid; i <= mb; i += blockDim.x) {
+        o_tok[i] = i == 0 ? 0 : (i == 1 ? mb : -1);
+        o_uni[i] = i == 0 ? 0 : (i == 1 ? U : -1);
+    }
+    for (int i = tid; i < Pb; i += blockDim.x) {
+        const int pg = p.t0 * p.k + i;
+        const int j = pslot[pg];
+        o_pslot[i] = j;
+        p.ids_out[i] = p.slot_of[j];
+        o_uexp[i] = i < U ? p.slot_of[i] : -1;
+        o_sp[i] = sp[s0 + i] - p.t0 * p.k;
+    }
+    for (int i = tid; i <= Pb; i += blockDim.x) o_spb[i] = i <= U ? spb[p.u0 + i] - s0 : -1;
+    if (tid == 0) o[0] = 1;
+}
+
 }  // namespace ffnq

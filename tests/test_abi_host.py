@@ -323,3 +323,40 @@ def test_layer_sandwich_refusals_and_query():
     assert call_sandwich(ffn(I8, I8, 256, 256), sh)[0] == -2    # INT4 experts only
     assert call_sandwich(f, ffn(I8, I8, 256, 384), sh_inter=512)[0] == -1   # shared shape mismatch
     assert call_sandwich(f, sh, ws=addr(60), ws_bytes=n - 256)[0] == -4
+
+
+def call_streamed(f, cache, E=8, hidden=256, inter=256, m=3, k=2, staging=addr(70), ws=None, ws_bytes=0):
+    L = fq.lib()
+    size = C.c_size_t(ws_bytes)
+    rc = L.ffnq_moe_routed_streamed(C.byref(f), E, hidden, inter, m, k, fq.ACT_SILU, addr(40), addr(41), addr(42),
+                                    addr(43), None, addr(50), None if cache is None else C.byref(cache), staging, ws,
+                                    C.byref(size), None)
+    return rc, size.value
+
+
+def test_streamed_refusals_and_query():
+    import numpy as np
+    T4 = fq.FMT_INT4_AFFINE_G64_TILED
+    t = fq.Ffn(fq.QMat(T4, 256, 256, addr(0), None, None), fq.QMat(T4, 256, 256, addr(10), None, None),
+               fq.QMat(T4, 256, 256, addr(20), None, None))
+    per = 3 * fq.packed_bytes(T4, 256, 256)
+    expert = np.full(4, -1, np.int32)
+    last = np.zeros(4, np.uint64)
+
+    def cache(n=4, nbytes=4 * per, slots=addr(80), table=True):
+        return fq.SlotCacheC(slots, nbytes, n, expert.ctypes.data if table else None, last.ctypes.data, 0, 0)
+
+    rc, n = call_streamed(t, cache())
+    assert rc == 0 and n > 0
+    assert call_streamed(t, cache(), m=0) == (0, 0)
+    assert call_streamed(t, None)[0] == -1
+    assert call_streamed(t, cache(), staging=None)[0] == -1
+    assert call_streamed(t, cache(n=0))[0] == -1
+    assert call_streamed(t, cache(nbytes=4 * per - 1))[0] == -1   # slots smaller than n_slots experts
+    assert call_streamed(t, cache(slots=addr(80) + 4))[0] == -1   # misaligned
+    assert call_streamed(t, cache(table=False))[0] == -1
+    expert[1] = 8                                                 # a slot naming an expert past n_experts
+    assert call_streamed(t, cache())[0] == -1
+    expert[1] = -1
+    assert call_streamed(ffn(I4, I4, 256, 256), cache())[0] == -2   # row-major experts: not streamed
+    assert call_streamed(t, cache(), ws=addr(60), ws_bytes=n - 256)[0] == -4
