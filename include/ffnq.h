@@ -311,7 +311,11 @@ FFNQ_API int ffnq_moe_route(const float* logits, const float* expert_scale, int 
  * seed:      device bf16 [m][hidden] (the gated shared expert) or NULL.
  * resid:     device bf16 [m][hidden], in/out.
  * Expert ids outside [0, n_experts) and plan entries outside their ranges are
- * skipped on the device rather than dereferenced.
+ * skipped on the device rather than dereferenced.  Contract: plan is the one
+ * ffnq_moe_route wrote for these topk_ids; the call cannot check a device
+ * plan on the host.  With any other plan the rows of tokens whose pairs it
+ * does not list are unspecified (never a fault); ffnq_moe_routed_streamed,
+ * which reads the plan back, refuses such a plan instead.
  */
 FFNQ_API int ffnq_moe_routed_batched(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter,
                             int m, int top_k, int act, const uint16_t* x,
