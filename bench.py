@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 KERNEL_SOURCES = tuple(f"moe_expert_dequant_amd/csrc/{f}" for f in
-                       ("device.h", "qgemm.h", "tiled.h", "route.h", "stream.h", "tail.h", "ffnq.hip"))
+                       ("device.h", "qgemm.h", "tiled.h", "route.h", "stream.h", "prefill.h", "tail.h", "ffnq.hip"))
 TRAFFIC_FILE = "profiles/traffic_gu_burst_kernel_int4_llama3-8b_m1.txt"
 
 

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libffnq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "ffnq.hip")]
-HEADERS = [os.path.join(CSRC, h) for h in ("device.h", "qgemm.h", "route.h", "stream.h", "tail.h", "tiled.h")] + [
+HEADERS = [os.path.join(CSRC, h) for h in ("device.h", "prefill.h", "qgemm.h", "route.h", "stream.h", "tail.h", "tiled.h")] + [
     os.path.join(ROOT, "include", "ffnq.h")]
 
 FLAGS = [

@@ -15,6 +15,7 @@
 #include "ffnq.h"
 #include "device.h"
 #include "qgemm.h"
+#include "prefill.h"
 #include "route.h"
 #include "stream.h"
 #include "tail.h"
@@ -744,11 +745,15 @@ struct RoutedWs {
     size_t act, part, seed, total;
 };
 
+int prefill_down_kg(int hidden, int moe_inter, long long u_est);
+
 RoutedWs routed_ws(int fmt, int hidden, int moe_inter, int m, int k, int n_experts)
 {
     RoutedWs w{};
     const size_t P = (size_t)m * k;
-    const int kg = down_ranges(fmt, moe_inter, hidden, m, false, rows_per_item(false, m, k, n_experts), false);
+    int kg = down_ranges(fmt, moe_inter, hidden, m, false, rows_per_item(false, m, k, n_experts), false);
+    if (is_tiled(fmt) && is_int4(fmt) && rows_per_item(false, m, k, n_experts) >= kBigRows)
+        kg = std::max(kg, prefill_down_kg(hidden, moe_inter, std::min<long long>((long long)P, n_experts)));
     size_t o = 0;
     w.act = o; o += align_up(2 * P * moe_inter * 2, 256);
     w.part = o; o += align_up((size_t)kg * P * hidden * sizeof(float), 256);
@@ -922,6 +927,121 @@ struct RouteIn {
     int cap;
 };
 
+// Prefill-sized routed items (prefill.h): the grouped kernels for the routed
+// gate/up and down when the experts are tiled INT4 and the pairs per union
+// entry reach kBigRows.  Rows per pass: 32 pairs for gate/up, 24 pairs (48
+// hi/lo rows) for down -- entries with more take further passes, row blocks
+// an entry leaves empty cost no MFMA; 4 code blocks per staged chunk (the
+// double-buffered rows then fit one CU's LDS); one tile per wave for gate/up,
+// and for down 2 where that keeps the grid's last round as full as 1 does.
+#ifndef FFNQ_PREFILL
+#define FFNQ_PREFILL 1
+#endif
+
+// Prefetch distance (steps of weights in flight per wave beyond the one being
+// multiplied), at least two, so that the wait for a step's weights never waits
+// for the activation rows staged after the previous step's loads.
+#ifndef FFNQ_PF_D_GU
+#define FFNQ_PF_D_GU 3
+#endif
+#ifndef FFNQ_PF_D_DN
+#define FFNQ_PF_D_DN 2   // two tiles per step: its scale/zero slots must fit the LDS beside 48 staged rows
+#endif
+
+// Waves per workgroup: 12 for gate/up (6 per matrix), 8 for down (at 4096
+// outputs, 12 would leave CUs without a unit).
+#ifndef FFNQ_PF_WAVES_GU
+#define FFNQ_PF_WAVES_GU 12
+#endif
+#ifndef FFNQ_PF_WAVES_DN
+#define FFNQ_PF_WAVES_DN 8
+#endif
+constexpr int kPfWavesGU = FFNQ_PF_WAVES_GU, kPfWavesDN = FFNQ_PF_WAVES_DN;
+#ifndef FFNQ_PF_TPW_GU
+#define FFNQ_PF_TPW_GU 1   // most tiles per gate/up wave (the registers of 12-wave workgroups hold one)
+#endif
+
+struct PrefillCfg {
+    bool ok;
+    int tpw_gu, tpw_dn, grid_gu, grid_dn, kg_dn;
+    size_t lds_gu, lds_dn;
+};
+
+// K ranges of the prefill down: enough (tile group, range) units for every CU
+// of a reference 256-CU part (device independent, so that the workspace size
+// is), at least 4 chunks of 512 inputs per range.
+constexpr int kPfTpwDn = 2;
+int prefill_down_kg(int hidden, int moe_inter, long long u_est)
+{
+    const TileGeo gd = tile_geo(FMT_INT4, hidden, moe_inter);
+    const long long units = u_est * ((gd.T + kPfWavesDN * kPfTpwDn - 1) / (kPfWavesDN * kPfTpwDn));
+    const int nch = (gd.nbk + 3) / 4;
+    int kg = (int)std::max<long long>(1, (kRefCUs + units - 1) / std::max<long long>(units, 1));
+    return std::max(1, std::min(kg, nch / 4));
+}
+
+// Tiles per wave: the most (up to `most`) for which the grid's last round is as
+// full as with fewer -- more tiles per unit amortise the staged rows.
+int prefill_tpw(int tiles, int waves_per_matrix, long long items, int cus, int most)
+{
+    auto eff = [&](int tpw) {
+        const long long per = (long long)waves_per_matrix * tpw;
+        const long long units = items * ((tiles + per - 1) / per);
+        const long long rounds = (units + cus - 1) / cus;
+        return (double)units / (double)(rounds * cus);
+    };
+    int best = 1;
+    for (int t = 2; t <= most; t *= 2)
+        if (eff(t) >= eff(best) - 1e-9) best = t;
+    return best;
+}
+
+PrefillCfg prefill_cfg(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int cus)
+{
+    PrefillCfg c{};
+    const int tf = FFNQ_FMT_INT4_AFFINE_G64_TILED;
+    if (!FFNQ_PREFILL || experts->gate.fmt != tf || experts->up.fmt != tf || experts->down.fmt != tf) return c;
+    if (rows_per_item(false, m, top_k, n_experts) < kBigRows) return c;
+    const long long u_est = std::min<long long>((long long)m * top_k, n_experts);
+    const TileGeo gg = tile_geo(FMT_INT4, moe_inter, hidden), gd = tile_geo(FMT_INT4, hidden, moe_inter);
+    c.tpw_gu = prefill_tpw(gg.T, kPfWavesGU / 2, u_est, cus, FFNQ_PF_TPW_GU);
+    c.tpw_dn = kPfTpwDn;
+    c.kg_dn = prefill_down_kg(hidden, moe_inter, u_est);
+    auto grid = [&](int tiles, int per, int kg) {
+        const long long units = u_est * ((tiles + per - 1) / per) * kg;
+        return (int)std::max<long long>(1, std::min<long long>(units, cus));
+    };
+    c.grid_gu = grid(gg.T, kPfWavesGU / 2 * c.tpw_gu, 1);
+    c.grid_dn = grid(gd.T, kPfWavesDN * c.tpw_dn, c.kg_dn);
+    c.lds_gu = (size_t)prefill_lds(kPfWavesGU, 2, 4, FFNQ_PF_D_GU, c.tpw_gu);
+    c.lds_dn = (size_t)prefill_lds(kPfWavesDN, 3, 4, FFNQ_PF_D_DN, c.tpw_dn);
+    c.ok = c.lds_gu <= kLdsMax && c.lds_dn <= kLdsMax;
+    return c;
+}
+
+#ifndef FFNQ_PF_SPS
+#define FFNQ_PF_SPS 2   // code blocks per step: two steps per 4-block chunk and tile
+#endif
+
+#define FFNQ_PF_CASE(DOWN_, W_, NMW_, RB_, TPW_, D_, EV)                                                     \
+    if (down == DOWN_ && tpw == TPW_) {                                                                       \
+        hipExtLaunchKernelGGL((prefill_kernel<W_, NMW_, RB_, 4, TPW_, D_, FFNQ_PF_SPS>), dim3(grid),          \
+                              dim3(64 * W_), lds, stream, phase_event(EV), phase_event(EV + 1), 0, q);       \
+        return hipGetLastError() == hipSuccess;                                                               \
+    }
+
+bool launch_prefill(bool down, int tpw, int grid, size_t lds, hipStream_t stream, const PrefillParams& prm)
+{
+    PrefillParams q = prm;
+    q.tpw = tpw;
+    FFNQ_PF_CASE(false, kPfWavesGU, 2, 2, 1, FFNQ_PF_D_GU, 0)
+#if FFNQ_PF_TPW_GU >= 2
+    FFNQ_PF_CASE(false, kPfWavesGU, 2, 2, 2, FFNQ_PF_D_GU, 0)
+#endif
+    FFNQ_PF_CASE(true, kPfWavesDN, 1, 3, kPfTpwDn, FFNQ_PF_D_DN, 2)
+    return false;
+}
+
 // Whether the routed gate/up launch routes the batch itself: every one of its
 // workgroups repeats the routing (ranking m * E keys), so only for batches
 // with few keys, where that costs less than a launch of its own.
@@ -1004,7 +1124,32 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     // hold (one per pair; several sub-batches may repeat an expert), those past
     // the plan's union return at once
     const int nr_items = P * ((moe_inter + 15) / 16);
-    if (rb.ok) {
+    const PrefillCfg pf = rb.ok ? PrefillCfg{} : prefill_cfg(experts, n_experts, hidden, moe_inter, m, top_k, cus);
+    PrefillParams pp{};
+    if (pf.ok) {
+        pp.tebytes = gp.tebytes;
+        pp.plan = plan;
+        pp.topk_ids = topk_ids;
+        pp.m = m;
+        pp.top_k = top_k;
+        pp.n_experts = n_experts;
+        pp.act = act;
+    }
+    if (pf.ok) {
+        if (sh) {
+            const int rc = launch_shared_gu(sh, hidden, m, act, x, gps, gcs, sb, stream);
+            if (rc != FFNQ_OK) return rc;
+        }
+        PrefillParams q = pp;
+        q.tq[0] = gp.tgate;
+        q.tq[1] = gp.tup;
+        q.N = moe_inter;
+        q.K = hidden;
+        q.src = x;
+        q.act_out = gp.act_out;
+        q.kg = 1;
+        if (!launch_prefill(false, pf.tpw_gu, pf.grid_gu, pf.lds_gu, stream, q)) return FFNQ_ERR_HIP;
+    } else if (rb.ok) {
         if (sh && sb.ok && to_fmt(sh->ffn->gate.fmt) == FMT_INT4 && sb.ks == rb.ks && sb.R == rb.R) {
             // shared and routed gate/up in one burst launch
             if (!launch_gu_burst_jobs(experts->gate.fmt, rb.R, rb.ks, std::max(sb.lds, rb.lds), gps,
@@ -1099,8 +1244,8 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     // partials, unchanged; one K range per workgroup) and both run in one launch.
     bool merged = false;
     KConfig dcs1 = dcs;
-    if (sh_part && tiled && is_tiled(sh->ffn->down.fmt) && is_int4(sh->ffn->down.fmt) && !dc.ts && dc.ks == 1 &&
-        dcs.nt == dc.nt && dcs.mt == dc.mt) {
+    if (!pf.ok && sh_part && tiled && is_tiled(sh->ffn->down.fmt) && is_int4(sh->ffn->down.fmt) && !dc.ts &&
+        dc.ks == 1 && dcs.nt == dc.nt && dcs.mt == dc.mt) {
         const TileGeo gs = tile_geo(FMT_INT4, hidden, sh->inter);
         dcs1.ts = 0;
         dcs1.ks = 1;
@@ -1135,7 +1280,19 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
         dp.tdown = static_cast<const uint8_t*>(experts->down.q);
         dp.tebytes = tiled_expert_bytes(experts->down);
     }
-    if (merged) {
+    int part_ranges = dc.kg;
+    if (pf.ok) {   // the grouped down: every pair's d as fp32 partials over kg K ranges
+        PrefillParams q = pp;
+        q.tq[0] = dp.tdown;
+        q.tebytes = dp.tebytes;   // the down matrices' own expert stride
+        q.N = hidden;
+        q.K = moe_inter;
+        q.src = gp.act_out;
+        q.part = dp.part;
+        q.kg = pf.kg_dn;
+        if (!launch_prefill(true, pf.tpw_dn, pf.grid_dn, pf.lds_dn, stream, q)) return FFNQ_ERR_HIP;
+        part_ranges = pf.kg_dn;
+    } else if (merged) {
         if (!launch_down_tiled2(dcs1, dps, dc, dp, stream)) return FFNQ_ERR_UNSUPPORTED;
     } else if (!(tiled ? launch_down_tiled(FMT_INT4, dc, stream, dp)
                        : launch_down(FMT_INT4, dc, u_est, hidden, stream, dp))) {
@@ -1146,7 +1303,7 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
     // seeded rank-ordered reduce + residual
     const long long total = (long long)m * hidden;
     const int rgrid = (int)std::min<long long>((total + 255) / 256, (long long)cus * 8);
-    hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, dc.kg, topk_w, topk_ids,
+    hipLaunchKernelGGL(moe_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, dp.part, part_ranges, topk_w, topk_ids,
                        n_experts, sh_part ? nullptr : seed_rows, resid, m, top_k, hidden, sh_part ? dps.part : nullptr,
                        sh_part ? dcs.kg : 0, sh_part ? dps.logit : nullptr);
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;

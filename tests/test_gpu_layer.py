@@ -126,6 +126,18 @@ def test_layer_union_past_experts(m, E, k, cap):
     assert rel_l2_rows(got, want) <= TOL
 
 
+@pytest.mark.parametrize("m,E,k", [(64, 8, 2), (96, 4, 1)])
+def test_layer_prefill_sized(m, E, k):
+    # 12 or more pairs per expert: the grouped prefill kernels for the routed
+    # phases beside the shared expert's own launches
+    hidden, inter, sh_inter, cap = 512, 256, 384, 32
+    say("layer prefill sized", m, E, k)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=4680 + m + E, shared_inter=sh_inter)
+    got, seed, ids, w = run_case(inp, E, hidden, inter, sh_inter, m, k, cap, gen.ACT_SILU, True, True)
+    want = oracle.moe_routed(inp["experts"], E, hidden, inter, gen.ACT_SILU, inp["x"], ids, w, seed, inp["resid"])
+    assert rel_l2_rows(got, want) <= TOL
+
+
 @pytest.mark.parametrize("tiled", [False, True])
 def test_layer_without_shared_is_unseeded_routed(tiled):
     hidden, inter, E, m, k, cap = 512, 256, 16, 3, 4, 8

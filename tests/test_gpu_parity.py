@@ -366,7 +366,8 @@ def test_routed_union_past_experts(m, E, k, cap, tiled):
 
 
 @LAYOUTS
-@pytest.mark.parametrize("m,E,k,use_seed", [(64, 8, 2, True), (64, 4, 1, False), (96, 8, 2, False)])
+@pytest.mark.parametrize("m,E,k,use_seed", [(64, 8, 2, True), (64, 4, 1, False), (96, 8, 2, False),
+                                            (160, 4, 1, True)])   # entries past one pass of 32 pairs
 def test_routed_prefill_sized(m, E, k, use_seed, tiled):
     hidden, inter, cap = 512, 1024, 32
     say("routed_prefill", m, E, k, use_seed, tiled)
