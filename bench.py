@@ -20,6 +20,13 @@ scaled by the same counters on a plain copy of known size; it is read from
 profiles/ and reported only while the kernel sources are the ones it was
 measured on, else null.
 
+Each roofline entry whose kernel streams 16 MB or more also carries
+`read_ceiling_GBs`: the rate a plain streaming-read kernel of the library
+(ffnq_stream_read) reaches for the same number of bytes on this GPU, read at
+successive offsets of a 1 GiB sweep so that nothing comes from the Infinity
+Cache -- the practical ceiling beside the published 8 TB/s (`read_ceiling`
+lists them).
+
 `value` is tokens/s over the wall clock of replays of a HIP graph that holds
 one call per weight copy (the host's launch cost is not the product's);
 per_m gives the eager per-call times (HIP events around each call).
@@ -482,6 +489,50 @@ def run_configs(steps: int, warmup: int) -> dict:
     return out
 
 
+READ_POOL = 1 << 30   # bytes swept by the read-rate probe before any byte is read again (4x the Infinity Cache)
+READ_MIN_BYTES = 16 << 20   # kernels that stream less than this are L2/Infinity-Cache latency cases
+
+
+def read_ceiling(sizes, steps: int = 30, warmup: int = 5) -> dict:
+    """The read rate a plain streaming-read kernel (ffnq_stream_read) reaches for each byte count: each launch
+    reads `size` bytes at the next offset of a 1 GiB sweep, timed by events the dispatch itself records.
+    Returns {size: (median us, GB/s)}."""
+    import torch
+    import moe_expert_dequant_amd as fq
+
+    sizes = sorted({int(b) // 16 * 16 for b in sizes if b >= 16})
+    if not sizes:
+        return {}
+    buf = torch.ones(READ_POOL + sizes[-1], dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for size in sizes:
+        stride = (size + 65535) // 65536 * 65536
+        slots = max(1, READ_POOL // stride)
+        evs = [fq.PhaseEvents() for _ in range(steps)]
+        for i in range(warmup + steps):
+            view = buf[(i % slots) * stride:(i % slots) * stride + size]
+            if i < warmup:
+                fq.stream_read(view, sink)
+                continue
+            with evs[i - warmup]:
+                fq.stream_read(view, sink)
+        torch.cuda.synchronize()
+        us = float(np.median([e.durations()[0] for e in evs])) * 1e3
+        out[size] = (us, size / (us * 1e-6) / 1e9)
+    del buf
+    return out
+
+
+def attach_read_ceiling(entries, rc: dict) -> None:
+    """Adds the plain-read rate for the same bytes to each roofline entry that streams from HBM."""
+    for e in entries:
+        b = int(e.get("algorithmic_bytes_per_launch", 0)) // 16 * 16
+        if b in rc:
+            e["read_ceiling_GBs"] = rc[b][1]
+            e["frac_of_read_ceiling"] = e["achieved"] / rc[b][1]
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -689,6 +740,14 @@ def main():
         out["configs"] = run_configs(100, 10)
         # every workload shape's gate/up and down kernels against their roofline
         out["roofline_kernels"] = [k for cf in out["configs"].values() for r in cf.values() for k in r.get("kernels", [])]
+    entries = ([out["roofline"]] if "roofline" in out else []) + out.get("roofline_kernels", [])
+    big = [e["algorithmic_bytes_per_launch"] for e in entries if e.get("algorithmic_bytes_per_launch", 0) >= READ_MIN_BYTES]
+    if big:
+        rc = read_ceiling(big)
+        attach_read_ceiling(entries, rc)
+        out["read_ceiling"] = [{"bytes": b, "us": v[0], "GBs": v[1], "frac_of_peak": v[1] / HBM_PEAK_GBS,
+                                "kernel": f"stream_read_kernel (256 x 512 threads, 16-byte loads)"}
+                               for b, v in sorted(rc.items())]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -473,6 +473,18 @@ FFNQ_API const char* ffnq_status_string(int status);
  * depend on this switch. */
 FFNQ_API int ffnq_set_phase_events(hipEvent_t* ev);
 
+/* ---- practical read rate (measurement aid) --------------------------------
+ * Not an operation of the method: a plain streaming read of `bytes` bytes of
+ * device memory at `buf` (16-byte loads, a fixed grid of 256 workgroups of
+ * 512 threads), so that a harness can set the weight-streaming kernels beside
+ * the read rate this GPU reaches for the same number of bytes, next to the
+ * published HBM peak.  `sink` (device, 4 bytes, 4-byte aligned) is almost
+ * never written; its contents mean nothing.  With ffnq_set_phase_events set,
+ * the launch takes ev[0]/ev[1].  Errors: INVALID (NULL pointers, buf not
+ * 16-byte aligned, bytes not a multiple of 16), HIP.  bytes == 0 enqueues
+ * nothing. */
+FFNQ_API int ffnq_stream_read(const void* buf, size_t bytes, unsigned* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

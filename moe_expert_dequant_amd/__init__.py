@@ -32,7 +32,7 @@ STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "WORKSP
 EXPORTS = ("ffnq_dense", "ffnq_dense_noalloc", "ffnq_shared_expert", "ffnq_router_logits", "ffnq_moe_route",
            "ffnq_moe_routed_batched",
            "ffnq_moe_layer", "ffnq_moe_layer_logits", "ffnq_moe_layer_sandwich", "ffnq_moe_routed_streamed",
-           "ffnq_status_string", "ffnq_set_phase_events", "ffnq_packed_bytes", "ffnq_pack")
+           "ffnq_status_string", "ffnq_set_phase_events", "ffnq_stream_read", "ffnq_packed_bytes", "ffnq_pack")
 
 
 def plan_ints(m: int, k: int) -> int:
@@ -93,6 +93,8 @@ def lib():
         L.ffnq_status_string.restype = C.c_char_p
         L.ffnq_set_phase_events.argtypes = [vp]
         L.ffnq_set_phase_events.restype = C.c_int
+        L.ffnq_stream_read.argtypes = [vp, C.c_size_t, vp, vp]
+        L.ffnq_stream_read.restype = C.c_int
         L.ffnq_packed_bytes.argtypes = [i32, i32, i32]
         L.ffnq_packed_bytes.restype = C.c_size_t
         L.ffnq_pack.argtypes = [C.POINTER(QMat), i32, vp, C.c_size_t, vp]
@@ -334,6 +336,14 @@ def to_device(mat: dict, device="cuda") -> dict:
             return torch.from_numpy(a.view(np.int16)).to(device)
         return torch.from_numpy(a).to(device)
     return dict(fmt=mat["fmt"], n=mat["n"], k=mat["k"], q=t(mat["q"]), s=t(mat["s"]), z=t(mat.get("z")))
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """ffnq_stream_read: a plain streaming read of the whole of `buf` (a CUDA
+    tensor, 16-byte aligned, a multiple of 16 bytes), for measuring the read
+    rate the GPU reaches; `sink` is a CUDA int32 tensor of at least one element."""
+    _check("ffnq_stream_read", lib().ffnq_stream_read(C.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                                      C.c_void_p(sink.data_ptr()), C.c_void_p(_stream(stream))))
 
 
 def packed_bytes(fmt: int, n: int, k: int) -> int:

@@ -21,6 +21,11 @@ constexpr int kRankMax = 256;        // experts up to which the top-k is found b
 constexpr int kLgCache = 4096;       // logits (m * E) staged in LDS before the top-k
 constexpr int kParPlan = 64;         // pairs from which the one-sub-batch plan is built in parallel
 constexpr int kPairPlan = 64;        // pairs up to which it is built one pair per thread, CSR included
+#ifndef FFNQ_KEY_RANK_MAX_E
+#define FFNQ_KEY_RANK_MAX_E 32
+#endif
+constexpr int kKeyRankMaxE = FFNQ_KEY_RANK_MAX_E;   // experts up to which the top-k takes a thread per key
+constexpr long long kKeyRankWeightWork = 16384;      // m * k * k bound of its thread-per-pair weights
 
 struct RouteParams {
     const float* logits;    // [m][E]
@@ -322,6 +327,43 @@ __global__ void __launch_bounds__(256) route_kernel(RouteParams p)
         for (int i = tid; i < m * E; i += blockDim.x) lg_s[i] = p.logits[i];
         __syncthreads();
     }
+    if (SMALL && E <= kKeyRankMaxE && (long long)m * k * k <= kKeyRankWeightWork) {
+        // Few experts per token: a thread per (token, expert) key counts the
+        // keys of its token above it, so that every token is ranked at once
+        // rather than a wave walking its tokens; ranks 0..k-1 name the top k.
+        for (int i = tid; i < m * E; i += blockDim.x) {
+            const int t = i / E, e = i - t * E;
+            const uint64_t key = route_key(lg_s[i], e);
+            const float* row = lg_s + t * E;
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2) rank += route_key(row[e2], e2) > key ? 1 : 0;
+            if (rank < k) ids_s[t * k + rank] = e;
+        }
+        __syncthreads();
+        // a thread per pair: the token's exponentials in rank order (NaN as
+        // -inf, -0 as +0, as the keys read them), their sum, its weight
+        for (int pp = tid; pp < m * k; pp += blockDim.x) {
+            const int t = pp / k, r_me = pp - t * k;
+            const float* row = lg_s + t * E;
+            const int* sel = ids_s + t * k;
+            auto logit = [&](int r) {
+                const float l = route_key_logit(route_key(row[sel[r]], 0));
+                return (l != l) ? -(double)INFINITY : (double)l;
+            };
+            const double l0 = logit(0);
+            double sum = 0.0, ex_me = 0.0;
+            for (int r = 0; r < k; ++r) {
+                const double lr = logit(r);
+                const double ex = (lr == l0) ? 1.0 : exp(lr - l0);
+                sum += ex;
+                if (r == r_me) ex_me = ex;
+            }
+            const int e = sel[r_me];
+            const double sc = p.scale ? (double)p.scale[e] : 1.0;
+            p.ids[pp] = e;
+            p.w[pp] = (float)(ex_me / sum * sc);
+        }
+    } else
     for (int t = w; t < m; t += nw) {
         uint64_t key[kMaxExperts / 64];
 #pragma unroll

@@ -360,3 +360,14 @@ def test_streamed_refusals_and_query():
     expert[1] = -1
     assert call_streamed(ffn(I4, I4, 256, 256), cache())[0] == -2   # row-major experts: not streamed
     assert call_streamed(t, cache(), ws=addr(60), ws_bytes=n - 256)[0] == -4
+
+
+def test_stream_read_refusals():
+    L = fq.lib()
+    vp = C.c_void_p
+    assert L.ffnq_stream_read(None, 64, vp(addr(1)), None) == -1
+    assert L.ffnq_stream_read(vp(addr(0)), 64, None, None) == -1
+    assert L.ffnq_stream_read(vp(addr(0) + 8), 64, vp(addr(1)), None) == -1   # buf not 16-byte aligned
+    assert L.ffnq_stream_read(vp(addr(0)), 72, vp(addr(1)), None) == -1       # not a multiple of 16
+    assert L.ffnq_stream_read(vp(addr(0)), 64, vp(addr(1) + 2), None) == -1   # sink not 4-byte aligned
+    assert L.ffnq_stream_read(vp(addr(0)), 0, vp(addr(1)), None) == fq.OK                 # nothing to read

@@ -256,7 +256,9 @@ def check_route(logits, k, cap, scale=None, label=""):
                                        (300, 8, 2, 32), (1000, 16, 4, 32), (1100, 16, 4, 32), (64, 128, 8, 32),
                                        # one pair per thread: ids written by several waves, read by all threads
                                        (2, 16, 4, 32), (4, 16, 8, 32), (8, 16, 8, 32), (8, 64, 4, 32),
-                                       (3, 128, 8, 32), (16, 8, 4, 32), (8, 128, 8, 32)])
+                                       (3, 128, 8, 32), (16, 8, 4, 32), (8, 128, 8, 32),
+                                       # a thread per key (few experts per token), and past its weight bound
+                                       (40, 12, 3, 6), (100, 32, 4, 32), (130, 31, 5, 9), (500, 8, 8, 32)])
 def test_route_random(m, E, k, cap):
     logits = gen.router_logits(gen.tensor_key(m * 1000 + E, k), m, E)
     check_route(logits, k, cap, label="random")
@@ -311,6 +313,13 @@ def test_route_ties_nan_inf_scale():
     check_route(lg, 3, 6, label="nan/inf")
     scale = (0.5 + rng.random(12)).astype(np.float32)
     check_route(lg, 3, 6, scale, label="scale")
+    # the same cases over more tokens than one workgroup ranks in its small-batch path
+    big = np.concatenate([lg, rng.integers(-2, 3, (48, 12)).astype(np.float32)])
+    big[20::5, 1::3] = np.nan
+    big[30, :] = np.inf
+    big[31, 4] = -0.0
+    check_route(big, 3, 6, label="nan/inf, 64 tokens")
+    check_route(big, 4, 32, scale, label="scale, 64 tokens")
 
 
 # ---------------------------------------------------------------------------
