@@ -332,7 +332,9 @@ def kernel_names(c: int, m: int):
     if m == 1:
         return ("gu_burst_kernel<INT4,1> (routed gate/up, routing)",
                 "moe_down_kernel<INT4,2,1> (routed down, reduce, residual)")
-    return "gu_tiled_kernel<INT4,...> (grouped bf16-MFMA gate/up)", "down_tiled_kernel<INT4,...> (grouped down)"
+    return ("prefill_kernel<12 waves, gate+up> (grouped bf16-MFMA gate/up + SiLU, staged K chunks)",
+            "prefill_kernel<8 waves, down> (grouped bf16-MFMA down, fp32 partials per K range; the reduction "
+            "with the residual is a launch of its own)")
 
 
 def kernel_phases(c: int, m: int, cfg: dict, call, n: int, union) -> list:

@@ -8,22 +8,27 @@
 // per expert (8 experts, 64 tokens, top 2: 11-23 pairs each) the activation
 // rows of an expert no longer fit the LDS over the whole K range, so:
 //
-//  * a workgroup of 8 waves owns one union entry and a run of tiles (each wave
-//    one matrix over TPW tiles, its own accumulators over the whole K range:
-//    no reduction; gate/up pairs a gate wave with an up wave on the same tiles);
+//  * a workgroup of W waves (12 for gate/up, 8 for down) owns one union entry
+//    and a run of tiles; each wave streams one matrix over TPW tiles with its
+//    own accumulators over its K range (no reduction inside the workgroup);
+//    gate/up splits the waves between the two matrices on the same tiles;
+//    down may split K into ranges whose fp32 partials the reduction adds;
 //  * K goes in chunks of CHB code blocks (128 inputs each); the chunk's rows of
 //    every pair of the entry (up to 16*RB rows per pass) are staged into LDS by
 //    direct global->LDS loads, double-buffered: chunk c+1 lands while chunk c
-//    is multiplied, one barrier per chunk;
-//  * every wave keeps D steps (a tile's scale/zero step and CHB code steps)
-//    of weights in flight beyond the one it multiplies; scale/zero steps go to
-//    wave-private LDS slots (their entries are read by row, which is not how
-//    the lanes hold them).
+//    is multiplied.  Each chunk opens with a barrier (its rows are in, the
+//    other buffer is free), then the workgroup forms every row's sum over each
+//    64-input group of the chunk (the zero point's term) and meets a second
+//    barrier;
+//  * every wave keeps D steps (a tile's scale/zero step and SPS code steps per
+//    tile) of weights in flight beyond the one it multiplies; scale/zero steps
+//    go to wave-private LDS slots (their entries are read by row, which is not
+//    how the lanes hold them).
 //
 // Same arithmetic as the other INT4 kernels: codes widened to bf16 128 + q, the
 // contraction on v_mfma_f32_16x16x32_bf16 with the activation rows as A, bias
-// and zero point removed through a ones-operand MFMA per 32 inputs, group
-// scales per 64 inputs, fp32 accumulation over K in increasing K order.
+// and zero point removed with the rows' group sums, group scales per 64
+// inputs, fp32 accumulation over K in increasing K order.
 // gate/up: f(g) * u is written as the bf16 hi/lo pair of each pair's act rows.
 // down: the rows are the pairs' hi/lo act rows; d = (hi-row sum) + (lo-row
 // sum) is written as the fp32 partial of the pair, summed by the reduction.
