@@ -647,8 +647,12 @@ DownParams dense_down_params(const ffnq_ffn* ffn, int hidden, int inter, int m, 
     return dp;
 }
 
+// With norm_part (RMSNorm tail only): the down projection's fp32 partials and
+// their count are handed back instead of launching the RMSNorm, for a caller
+// that folds the norm into a kernel of its own.
 int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, int act, int tail, const uint16_t* x,
-              uint16_t* out, const uint16_t* aux, float eps, void* ws, hipStream_t stream)
+              uint16_t* out, const uint16_t* aux, float eps, void* ws, hipStream_t stream,
+              const float** norm_part = nullptr, int* norm_R = nullptr)
 {
     const int cus = device_cus();
     unsigned char* base = static_cast<unsigned char*>(ws);
@@ -689,7 +693,10 @@ int run_dense(bool shared, const ffnq_ffn* ffn, int hidden, int inter, int m, in
     }
     if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
 
-    if (tail == FFNQ_TAIL_RMSNORM) {
+    if (tail == FFNQ_TAIL_RMSNORM && norm_part) {
+        *norm_part = dp.part;
+        *norm_R = kg;
+    } else if (tail == FFNQ_TAIL_RMSNORM) {
         const size_t row_lds = hidden <= kRowLds ? (size_t)hidden * 6 : 0;
         hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(kNormThreads), row_lds, stream, dp.part, kg, m, aux, out, hidden,
                            eps);
@@ -1061,8 +1068,18 @@ bool route_in_gu(const ffnq_ffn* experts, int n_experts, int hidden, int moe_int
 int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter, int m, int top_k, int act,
                const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const int32_t* plan,
                const uint16_t* seed, uint16_t* resid, unsigned char* base, hipStream_t stream, const LayerShared* sh,
-               const RouteIn* rin = nullptr)
+               const RouteIn* rin = nullptr, bool out_zero = false)
 {
+    // out_zero: the rows are written as the sum on +0 (their contents on entry
+    // do not matter) -- in the fused down directly, else by zeroing them first
+    if (out_zero && !moe_down_cfg(experts, n_experts, hidden, moe_inter, m, top_k, sh ? sh->ffn : nullptr,
+                                  sh ? sh->inter : 0).ok) {
+        const size_t nrow = (size_t)m * hidden;
+        hipLaunchKernelGGL(zero_u16_kernel, dim3((unsigned)std::min<size_t>((nrow + 255) / 256, 1024)), dim3(256), 0,
+                           stream, resid, nrow);
+        if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+        out_zero = false;
+    }
     const RoutedWs L = routed_ws(experts->down.fmt, hidden, moe_inter, m, top_k, n_experts);
     const int cus = device_cus();
     const int P = m * top_k;
@@ -1203,6 +1220,7 @@ int run_routed(const ffnq_ffn* experts, int n_experts, int hidden, int moe_inter
             q.seed = seed;
         }
         q.resid = resid;
+        q.resid_zero = out_zero ? 1 : 0;
         if (!launch_moe_down(md, hidden, stream, q)) return FFNQ_ERR_UNSUPPORTED;
         return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
     }
@@ -1472,18 +1490,20 @@ int moe_layer_sandwich(const ffnq_ffn* experts, int n_experts, int hidden, int m
         if (rc != FFNQ_OK) return rc;
         rin = nullptr;
     }
+    // the shared branch up to its down projection's partials; its RMSNorm runs
+    // in the tail kernel
+    const float* sh_part = nullptr;
+    int sh_R = 0;
     rc = run_dense(true, shared, hidden, shared_inter, m, act, FFNQ_TAIL_RMSNORM, x, h1, shared_norm_w, eps,
-                   base + L.sh, stream);
+                   base + L.sh, stream, &sh_part, &sh_R);
     if (rc != FFNQ_OK) return rc;
-    const size_t nrow = (size_t)m * hidden;
-    hipLaunchKernelGGL(zero_u16_kernel, dim3((unsigned)std::min<size_t>((nrow + 255) / 256, 1024)), dim3(256), 0,
-                       stream, r, nrow);
-    if (hipGetLastError() != hipSuccess) return FFNQ_ERR_HIP;
+    // the routed sum from +0 into r
     rc = run_routed(experts, n_experts, hidden, moe_inter, m, top_k, act, x, topk_ids, topk_w, plan, nullptr, r,
-                    base + L.routed, stream, nullptr, rin);
+                    base + L.routed, stream, nullptr, rin, true);
     if (rc != FFNQ_OK) return rc;
-    hipLaunchKernelGGL(sandwich_tail_kernel, dim3(m), dim3(kTailThreads), 0, stream, h1, r, post_norm_w, hidden, eps,
-                       resid);
+    const size_t tail_lds = hidden <= kRowLds ? (size_t)hidden * 8 : (size_t)hidden * 2;
+    hipLaunchKernelGGL(sandwich_norm_tail_kernel, dim3(m), dim3(kNormThreads), tail_lds, stream, sh_part, sh_R, m,
+                       shared_norm_w, r, post_norm_w, hidden, eps, resid);
     return hipGetLastError() == hipSuccess ? FFNQ_OK : FFNQ_ERR_HIP;
 }
 

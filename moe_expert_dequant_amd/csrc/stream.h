@@ -470,6 +470,7 @@ struct MoeDownParams {
     const float* sh_logit;    // its gate logits [m]
     const uint16_t* seed;     // bf16 [m][N] (no shared expert), or null for a zero seed
     uint16_t* resid;          // bf16 [m][N], in/out
+    int resid_zero;           // 1: resid is written as bf16(+0 + acc); its contents on entry are not read
     int ks;                   // waves per workgroup
     int max_units;            // reduction slots: units of the largest union the plan can hold
 };
@@ -619,7 +620,7 @@ __global__ void __launch_bounds__(1024) moe_down_kernel(MoeDownParams p)
         acc0 = __fadd_rn(acc0, __fmul_rn(tw[pr], d));
     }
     uint16_t* o = p.resid + (size_t)t * p.N + n;
-    *o = bf16_from_f64((double)bf16_f32(*o) + (double)acc0);
+    *o = bf16_from_f64((p.resid_zero ? 0.0 : (double)bf16_f32(*o)) + (double)acc0);
 }
 
 }  // namespace ffnq

@@ -57,14 +57,15 @@ __device__ __forceinline__ float sum_parts8(const float* part, int R, size_t str
 constexpr int kRowLds = 8192;
 constexpr int kNormThreads = 1024;
 
-__global__ void __launch_bounds__(kNormThreads) rmsnorm_kernel(const float* __restrict__ part, int R, int m,
-                                                               const uint16_t* __restrict__ w,
-                                                               uint16_t* __restrict__ out, int n, float eps)
+// One row t of the RMSNorm, by a workgroup of kNormThreads; store(i, v)
+// receives every rounded value.  hrow/wrow: the dynamic LDS row (used when
+// n <= kRowLds); partial: kNormThreads / 64 doubles of LDS.
+template <class Store>
+__device__ __forceinline__ void rmsnorm_row(const float* __restrict__ part, int R, int m,
+                                            const uint16_t* __restrict__ w, int n, float eps, int t, float* hrow,
+                                            uint16_t* wrow, double* partial, Store store)
 {
-    extern __shared__ float hrow[];   // [n] summed row, then [n] bf16 weight
-    uint16_t* wrow = (uint16_t*)(hrow + n);
-    __shared__ double partial[kNormThreads / 64];
-    const int t = blockIdx.x, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     const size_t stride = (size_t)m * n;
     const bool held = n <= kRowLds;
     double ss = 0.0;
@@ -117,8 +118,19 @@ __global__ void __launch_bounds__(kNormThreads) rmsnorm_kernel(const float* __re
     for (int i = tid; i < n; i += blockDim.x) {
         const double h = held ? (double)hrow[i] : (double)sum_parts(part, R, stride, (size_t)t * n + i);
         const uint16_t wi = held ? wrow[i] : w[i];
-        out[(size_t)t * n + i] = bf16_from_f64(h * r * (double)bf16_f32(wi));
+        store(i, bf16_from_f64(h * r * (double)bf16_f32(wi)));
     }
+}
+
+__global__ void __launch_bounds__(kNormThreads) rmsnorm_kernel(const float* __restrict__ part, int R, int m,
+                                                               const uint16_t* __restrict__ w,
+                                                               uint16_t* __restrict__ out, int n, float eps)
+{
+    extern __shared__ float hrow[];   // [n] summed row, then [n] bf16 weight
+    __shared__ double partial[kNormThreads / 64];
+    const int t = blockIdx.x;
+    rmsnorm_row(part, R, m, w, n, eps, t, hrow, (uint16_t*)(hrow + n), partial,
+                [&](int i, uint16_t v) { out[(size_t)t * n + i] = v; });
 }
 
 // Dense tails after a K-split down projection: raw residual add
@@ -214,36 +226,42 @@ __global__ void __launch_bounds__(256) zero_u16_kernel(uint16_t* __restrict__ p,
 
 // The Gemma-style sandwich tail ([qwen/moe_batch.rs] module doc, first
 // bullet: the routed sum starts from zero and the shared branch, normed by
-// its own post-FFN RMSNorm, joins in the layer's sandwich tail).  Per token t
-// (one workgroup): z = h1 + r (the bf16 shared row and the bf16 routed row,
-// added in double, exactly), n = bf16(z / sqrt(mean(z^2) + eps) * w) with the
-// sum of squares, the scale and the product in double, and one raw residual
-// add resid = bf16(resid + n).
-constexpr int kTailThreads = 256;
-
-__global__ void __launch_bounds__(kTailThreads) sandwich_tail_kernel(const uint16_t* __restrict__ h1,
-                                                                     const uint16_t* __restrict__ r,
-                                                                     const uint16_t* __restrict__ w, int n, float eps,
-                                                                     uint16_t* __restrict__ resid)
+// its own post-FFN RMSNorm, joins in the layer's sandwich tail), with that
+// RMSNorm in the same launch.  Per token t (one workgroup of kNormThreads):
+// h1 = the shared expert's RMSNorm row from its down projection's partials
+// (rmsnorm_row, the arithmetic of rmsnorm_kernel, so h1 is bit for bit what
+// ffnq_shared_expert writes), kept in LDS; z = h1 + r (the bf16 shared row and
+// the bf16 routed row, added in double, exactly), n = bf16(z / sqrt(mean(z^2)
+// + eps) * w) with the sum of squares, the scale and the product in double,
+// and one raw residual add resid = bf16(resid + n).  Dynamic LDS: n * 8 bytes
+// when n <= kRowLds (the summed row, the weight, h1), else n * 2 (h1).
+__global__ void __launch_bounds__(kNormThreads) sandwich_norm_tail_kernel(
+    const float* __restrict__ part, int R, int m, const uint16_t* __restrict__ shared_w, const uint16_t* __restrict__ r,
+    const uint16_t* __restrict__ w, int n, float eps, uint16_t* __restrict__ resid)
 {
-    __shared__ double partial[kTailThreads / 64];
+    extern __shared__ float hrow[];
+    const bool held = n <= kRowLds;
+    uint16_t* wrow = (uint16_t*)(hrow + (held ? n : 0));
+    uint16_t* h1 = held ? wrow + n : (uint16_t*)hrow;
+    __shared__ double partial[kNormThreads / 64];
     const int t = blockIdx.x, tid = threadIdx.x;
-    const uint16_t* ht = h1 + (size_t)t * n;
+    rmsnorm_row(part, R, m, shared_w, n, eps, t, hrow, wrow, partial, [&](int i, uint16_t v) { h1[i] = v; });
+    __syncthreads();   // h1 is in; partial is free again
     const uint16_t* rt = r + (size_t)t * n;
     double ss = 0.0;
-    for (int i = tid; i < n; i += kTailThreads) {
-        const double z = (double)bf16_f32(ht[i]) + (double)bf16_f32(rt[i]);
+    for (int i = tid; i < n; i += kNormThreads) {
+        const double z = (double)bf16_f32(h1[i]) + (double)bf16_f32(rt[i]);
         ss += z * z;
     }
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     if ((tid & 63) == 0) partial[tid >> 6] = ss;
     __syncthreads();
     double tot = 0.0;
-    for (int i = 0; i < kTailThreads / 64; ++i) tot += partial[i];
+    for (int i = 0; i < kNormThreads / 64; ++i) tot += partial[i];
     const double inv = 1.0 / sqrt(tot / (double)n + (double)eps);
     uint16_t* o = resid + (size_t)t * n;
-    for (int i = tid; i < n; i += kTailThreads) {
-        const double z = (double)bf16_f32(ht[i]) + (double)bf16_f32(rt[i]);
+    for (int i = tid; i < n; i += kNormThreads) {
+        const double z = (double)bf16_f32(h1[i]) + (double)bf16_f32(rt[i]);
         const uint16_t nb = bf16_from_f64(z * inv * (double)bf16_f32(w[i]));
         o[i] = bf16_from_f64((double)bf16_f32(o[i]) + (double)bf16_f32(nb));
     }
