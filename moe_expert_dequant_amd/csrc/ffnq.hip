@@ -1350,7 +1350,7 @@ int check_route(const float* logits, const float* expert_scale, int m, int n_exp
 
 // A checked route with m > 0: the small-batch kernel when the batch has at most
 // 256 keys (one workgroup, a thread per key; measured faster there, slower
-// than route_kernel's wave per token at 512 keys), else route_kernel.
+// than route_kernel at 512 keys), else route_kernel.
 constexpr int kSmallRouteKeys = 256;
 int launch_route(const float* logits, const float* expert_scale, int m, int n_experts, int top_k, int slot_cap,
                  int32_t* topk_ids, float* topk_w, int32_t* plan, hipStream_t stream)

@@ -5,9 +5,10 @@
 // read_f32_buffer_at + router_topk_gemma4), then plan sub-batches whose expert
 // union fits the slot cap (next_routed_sub_batch / plan_and_stream_union).
 // Here both steps run in one workgroup so the layer has no host round trip:
-// the waves select each token's experts in parallel, then the greedy union
-// plan is built -- in parallel when the whole batch's union fits the cap (one
-// sub-batch), else by wave 0 walking the tokens in order.  The router GEMV
+// the tokens' experts are selected in parallel (a thread per (token, expert)
+// key when a token has few experts, else a wave per token), then the greedy
+// union plan is built -- in parallel when the whole batch's union fits the cap
+// (one sub-batch), else by wave 0 walking the tokens in order.  The router GEMV
 // that produces the logits (router_gemv_kernel) is a launch of its own.
 #pragma once
 #include "device.h"
