@@ -538,3 +538,18 @@ def test_config4_mixtral_moe(m, resid_kind, tiled):
     check(got, want, f"config4 m {m} resid {resid_kind}")
     counts = np.bincount(ids.ravel(), minlength=c["n_experts"])
     say(f"config4 m {m} tokens per expert min {counts.min()} max {counts.max()}")
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_shared_expert_rmsnorm_row_past_lds(m):
+    # hidden 8320 > 8192: the RMSNorm keeps no row in LDS and reads the
+    # partials twice (the second pass re-sums them)
+    hidden, inter = 8320, 256
+    say("shared rmsnorm wide row", m)
+    for fmt in (I8, I4):
+        inp = gen.dense_inputs(hidden, inter, m, fmt, seed=2600 + m + fmt, row_scales=True)
+        want = oracle.shared_expert(inp["ffn"], hidden, inter, gen.ACT_GELU_TANH, gen.TAIL_RMSNORM, inp["x"],
+                                    inp["norm_w"])
+        got = gpu_dense(inp, hidden, inter, gen.ACT_GELU_TANH, gen.TAIL_RMSNORM, shared=True, aux=inp["norm_w"],
+                        tiled=True)
+        check(got, want, f"shared rmsnorm wide row fmt {fmt} m {m}")

@@ -96,3 +96,14 @@ def test_sandwich_workload(m):
     inp = gen.config_inputs(5, m, row_scales=True)
     run_case(inp, c["n_experts"], c["hidden"], c["moe_inter"], c["shared_inter"], m, c["top_k"], c["cap"], True,
              f"sandwich workload m {m}")
+
+
+@pytest.mark.parametrize("m", [1, 5])
+def test_sandwich_row_past_lds(m):
+    # hidden 8320 > 8192: the fused tail holds only h1 in LDS and reads the
+    # shared branch's partials twice; m = 5 takes the down path that zeroes r
+    hidden, inter, sh_inter, E, k, cap = 8320, 256, 256, 8, 2, 8
+    say("sandwich wide row", m)
+    inp = gen.sandwich_inputs(hidden, E, inter, m, seed=5300 + m, shared_inter=sh_inter, shared_fmt=I8,
+                              row_scales=True)
+    run_case(inp, E, hidden, inter, sh_inter, m, k, cap, True, f"sandwich wide row m {m}")
