@@ -1,0 +1,87 @@
+"""Seeded random shapes through ffnq_moe_layer_logits, against the oracle's
+chain for the same layer: oracle.moe_route (ids and plan bit for bit, weights
+within fp32 rounding), the shared expert's sigmoid-gated seed, then the routed
+half seeded with it.  The shapes are drawn so that every launch plan of the
+layer appears across the cases: routing inside the gate/up launch or before
+it, the fused down (m <= 4) or the per-pair partials and the reduction, caps
+that split the batch, tiled and row-major weights, and the grouped prefill
+kernels (12 or more pairs per expert)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import moe_expert_dequant_amd as fq
+import oracle
+from helpers import rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+N_CASES = 24
+
+
+def draw(i):
+    r = np.random.default_rng(9000 + i)
+    hidden = int(r.choice([256, 384, 512, 640, 1024]))
+    inter = int(r.choice([128, 256, 384, 640]))
+    if i % 6 == 5:   # prefill-sized: few experts, many tokens
+        E, k, m = int(r.choice([4, 6, 8])), int(r.choice([1, 2])), int(r.integers(48, 97))
+    else:
+        E = int(r.integers(4, 41))
+        k = int(r.integers(1, min(8, E) + 1))
+        m = int(r.choice([1, 2, 3, 4, 5, 8, 13, 24]))
+    cap = int(r.integers(k, 33))
+    sh_inter = int(r.choice([0, 256, 384]))
+    tiled = bool(r.integers(0, 4) > 0)
+    act = int(r.choice([gen.ACT_SILU, gen.ACT_GELU_TANH]))
+    scaled = bool(r.integers(0, 3) == 0)
+    return hidden, inter, E, k, m, cap, sh_inter, tiled, act, scaled
+
+
+def dev16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def mats(f, tiled, n_experts=1):
+    d = {n: fq.to_device(f[n]) for n in ("gate", "up", "down")}
+    if tiled:
+        d = {n: fq.pack(d[n], n_experts) for n in d}
+    return d, fq.ffn_struct(d)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_layer_logits_random(i):
+    hidden, inter, E, k, m, cap, sh_inter, tiled, act, scaled = draw(i)
+    print("[case] fuzz", i, dict(hidden=hidden, inter=inter, E=E, k=k, m=m, cap=cap, sh_inter=sh_inter,
+                                 tiled=tiled, act=act, scaled=scaled), flush=True)
+    inp = gen.moe_inputs(hidden, E, inter, m, seed=9100 + i, shared_inter=sh_inter)
+    scale = (0.5 + np.random.default_rng(9200 + i).random(E)).astype(np.float32) if scaled else None
+    ex_d, ex = mats(inp["experts"], tiled, E)   # device tensors stay referenced while their structs are used
+    sh_d, sh = mats(inp["shared"], tiled) if sh_inter else (None, None)
+    gate = dev16(inp["gate_vec"]) if sh_inter else None
+    resid = dev16(inp["resid"])
+    ids = torch.full((m, k), -9, dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.full((fq.plan_ints(m, k),), -9, dtype=torch.int32, device="cuda")
+    fq.moe_layer_logits(ex, E, hidden, inter, m, k, act, sh, sh_inter, gate, dev16(inp["x"]),
+                        dev(inp["logits"].astype(np.float32)), cap, ids, w, plan, resid,
+                        expert_scale=None if scale is None else dev(scale))
+    torch.cuda.synchronize()
+
+    rc, ids_o, w_o, plan_o = oracle.moe_route(inp["logits"], k, cap, scale)
+    assert rc == 0
+    assert np.array_equal(ids.cpu().numpy(), ids_o) and np.array_equal(plan.cpu().numpy(), plan_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=1e-6, atol=1e-30)
+    seed = None
+    if sh_inter:
+        seed = oracle.shared_expert(inp["shared"], hidden, sh_inter, act, gen.TAIL_SIGMOID_GATE, inp["x"],
+                                    inp["gate_vec"])
+    want = oracle.moe_routed(inp["experts"], E, hidden, inter, act, inp["x"], ids_o, w_o, seed, inp["resid"])
+    got = resid.cpu().numpy().view(np.uint16)
+    err = rel_l2_rows(got, want)
+    assert err <= TOL, (i, err)
