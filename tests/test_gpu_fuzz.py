@@ -1,11 +1,14 @@
-"""Seeded random shapes through ffnq_moe_layer_logits, against the oracle's
-chain for the same layer: oracle.moe_route (ids and plan bit for bit, weights
-within fp32 rounding), the shared expert's sigmoid-gated seed, then the routed
-half seeded with it.  The shapes are drawn so that every launch plan of the
-layer appears across the cases: routing inside the gate/up launch or before
-it, the fused down (m <= 4) or the per-pair partials and the reduction, caps
-that split the batch, tiled and row-major weights, and the grouped prefill
-kernels (12 or more pairs per expert)."""
+"""Seeded random shapes against the oracle.
+
+ffnq_moe_layer_logits against the oracle's chain for the same layer:
+oracle.moe_route (ids and plan bit for bit, weights within fp32 rounding), the
+shared expert's sigmoid-gated seed, then the routed half seeded with it.  The
+shapes are drawn so that every launch plan of the layer appears across the
+cases: routing inside the gate/up launch or before it, the fused down
+(m <= 4) or the per-pair partials and the reduction, caps that split the
+batch, tiled and row-major weights, and the grouped prefill kernels (12 or
+more pairs per expert).  Then ffnq_dense and ffnq_shared_expert over random
+widths, token counts, format pairs, activations, tails and layouts."""
 import numpy as np
 import pytest
 import torch
@@ -83,5 +86,51 @@ def test_layer_logits_random(i):
                                     inp["gate_vec"])
     want = oracle.moe_routed(inp["experts"], E, hidden, inter, act, inp["x"], ids_o, w_o, seed, inp["resid"])
     got = resid.cpu().numpy().view(np.uint16)
+    err = rel_l2_rows(got, want)
+    assert err <= TOL, (i, err)
+
+
+# ---------------------------------------------------------------------------
+# the dense FFN and the shared expert: random widths, token counts, formats
+# (gate/up and down independently), activations, tails and layouts, with a
+# zero residual every other case so that the bar applies to h itself
+
+def draw_dense(i):
+    r = np.random.default_rng(9500 + i)
+    hidden = int(r.choice([128, 256, 384, 640, 1024, 1536]))
+    inter = int(r.choice([128, 256, 384, 896, 1408]))
+    m = int(r.choice([1, 2, 3, 4, 5, 7, 8, 11, 16, 33]))
+    fmt = int(r.choice([gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64]))
+    fmt_down = int(r.choice([gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64]))
+    act = int(r.choice([gen.ACT_SILU, gen.ACT_GELU_TANH]))
+    shared = bool(r.integers(0, 2))
+    tail = int(r.choice([gen.TAIL_NONE, gen.TAIL_RMSNORM, gen.TAIL_SIGMOID_GATE])) if shared else gen.TAIL_RESIDUAL
+    tiled = bool(r.integers(0, 3) > 0)
+    zero_resid = bool(i % 2)
+    return hidden, inter, m, fmt, fmt_down, act, shared, tail, tiled, zero_resid
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_dense_random(i):
+    hidden, inter, m, fmt, fmt_down, act, shared, tail, tiled, zero_resid = draw_dense(i)
+    print("[case] dense fuzz", i, dict(hidden=hidden, inter=inter, m=m, fmt=fmt, fmt_down=fmt_down, act=act,
+                                       shared=shared, tail=tail, tiled=tiled, zero_resid=zero_resid), flush=True)
+    inp = gen.dense_inputs(hidden, inter, m, fmt, seed=9600 + i, fmt_down=fmt_down, row_scales=True)
+    if zero_resid:
+        inp["resid"] = np.zeros_like(inp["resid"])
+    aux = {gen.TAIL_NONE: None, gen.TAIL_RESIDUAL: None, gen.TAIL_RMSNORM: inp["norm_w"],
+           gen.TAIL_SIGMOID_GATE: inp["gate_vec"]}[tail]
+    d, st = mats(inp["ffn"], tiled)
+    x = dev16(inp["x"])
+    if shared:
+        out = torch.zeros((m, hidden), dtype=torch.int16, device="cuda")
+        fq.shared_expert(st, hidden, inter, m, act, tail, x, out, None if aux is None else dev16(aux), 1e-6)
+        want = oracle.shared_expert(inp["ffn"], hidden, inter, act, tail, inp["x"], aux)
+    else:
+        out = dev16(inp["resid"])
+        fq.dense(st, hidden, inter, m, act, tail, x, out, None, 1e-6)
+        want = oracle.dense(inp["ffn"], hidden, inter, act, tail, inp["x"], inp["resid"])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
     err = rel_l2_rows(got, want)
     assert err <= TOL, (i, err)
