@@ -8,7 +8,8 @@ cases: routing inside the gate/up launch or before it, the fused down
 (m <= 4) or the per-pair partials and the reduction, caps that split the
 batch, tiled and row-major weights, and the grouped prefill kernels (12 or
 more pairs per expert).  Then ffnq_dense and ffnq_shared_expert over random
-widths, token counts, format pairs, activations, tails and layouts."""
+widths, token counts, format pairs, activations, tails and layouts, and
+ffnq_moe_layer_sandwich over random shapes against the oracle's layer."""
 import numpy as np
 import pytest
 import torch
@@ -133,4 +134,52 @@ def test_dense_random(i):
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint16)
     err = rel_l2_rows(got, want)
+    assert err <= TOL, (i, err)
+
+
+# ---------------------------------------------------------------------------
+# the Gemma-style sandwich layer: random shapes, shared-branch formats and
+# expert scales, against the oracle's layer step by step
+
+def draw_sandwich(i):
+    r = np.random.default_rng(9800 + i)
+    hidden = int(r.choice([256, 384, 512, 1024]))
+    inter = int(r.choice([128, 256, 384]))
+    sh_inter = int(r.choice([128, 256, 640]))
+    E = int(r.integers(4, 33))
+    k = int(r.integers(1, min(8, E) + 1))
+    m = int(r.choice([1, 2, 3, 4, 6, 9, 17]))
+    cap = int(r.integers(k, 33))
+    sh_fmt = int(r.choice([gen.FMT_INT8_ROW, gen.FMT_INT4_AFFINE_G64]))
+    scaled = bool(r.integers(0, 2))
+    tiled = bool(r.integers(0, 4) > 0)
+    return hidden, inter, sh_inter, E, k, m, cap, sh_fmt, scaled, tiled
+
+
+@pytest.mark.parametrize("i", range(N_CASES // 2))
+def test_sandwich_random(i):
+    hidden, inter, sh_inter, E, k, m, cap, sh_fmt, scaled, tiled = draw_sandwich(i)
+    print("[case] sandwich fuzz", i, dict(hidden=hidden, inter=inter, sh_inter=sh_inter, E=E, k=k, m=m, cap=cap,
+                                          sh_fmt=sh_fmt, scaled=scaled, tiled=tiled), flush=True)
+    act, eps = gen.ACT_GELU_TANH, 1e-6
+    inp = gen.sandwich_inputs(hidden, E, inter, m, seed=9900 + i, shared_inter=sh_inter, shared_fmt=sh_fmt,
+                              row_scales=True)
+    sc = inp["expert_scale"] if scaled else None
+    rc, ids_o, w_o, plan_o, h1_o, r_o, out_o = oracle.moe_sandwich_layer(
+        inp["experts"], E, hidden, inter, act, inp["shared"], sh_inter, inp["shared_norm_w"], inp["post_norm_w"], eps,
+        inp["x"], inp["logits"], sc, k, cap, inp["resid"])
+    assert rc == 0
+    ex_d, ex = mats(inp["experts"], tiled, E)
+    sh_d, sh = mats(inp["shared"], tiled)
+    resid = dev16(inp["resid"])
+    ids = torch.full((m, k), -9, dtype=torch.int32, device="cuda")
+    w = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    plan = torch.full((fq.plan_ints(m, k),), -9, dtype=torch.int32, device="cuda")
+    fq.moe_layer_sandwich(ex, E, hidden, inter, m, k, act, sh, sh_inter, dev16(inp["shared_norm_w"]),
+                          dev16(inp["post_norm_w"]), eps, dev16(inp["x"]), dev(inp["logits"].astype(np.float32)), cap,
+                          ids, w, plan, resid, expert_scale=None if sc is None else dev(sc))
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_o) and np.array_equal(plan.cpu().numpy(), plan_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=1e-6, atol=1e-30)
+    err = rel_l2_rows(resid.cpu().numpy().view(np.uint16), out_o)
     assert err <= TOL, (i, err)
